@@ -1,0 +1,21 @@
+"""libinkattn for MI355X (gfx950): the Inkling attention-block hot path.
+
+* ``inkattn_sconv``            -- window-4 short convolution of keys and values
+                                 fused with the paged KV-cache write and the
+                                 three-token state update;
+* ``inkattn_relattn_prefill``  -- relative-position GQA attention over new
+                                 tokens (bf16/fp32 MFMA, sheared bias band);
+* ``inkattn_relattn_decode``   -- split-K paged decode plus log-sum-exp merge.
+
+The functions mirror the C ABI in ``include/inkattn.h`` one to one and take
+torch device tensors (torch supplies memory and streams only).  The helpers in
+``kvcache`` allocate the cache in the library's layout.
+"""
+
+from ._lib import (  # noqa: F401
+    BF16, FP32, OK, EINVAL, ENOTSUP, EHIP, EXPORTED, LIB_PATH,
+    AttnDesc, InkattnError, make_desc, status_string,
+    inkattn_sconv, inkattn_relattn_prefill, inkattn_relattn_decode,
+    inkattn_relattn_decode_num_splits, inkattn_relattn_decode_workspace_size,
+)
+from . import kvcache  # noqa: F401

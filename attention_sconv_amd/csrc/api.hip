@@ -1,0 +1,163 @@
+// C-ABI layer of libinkattn: argument validation, split-count heuristic,
+// workspace sizing, and dispatch to the kernel launchers.  Declarations and
+// the meaning of every argument are in include/inkattn.h.
+#include "inkattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+
+using inkattn::AttnShape;
+
+namespace {
+
+constexpr int kCUs = 256;                  // MI355X compute units
+constexpr int kDecodeTargetGroups = 4 * kCUs;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inkattn_status_t check_desc(const inkattn_attn_desc_t* d) {
+  if (!d) return INKATTN_EINVAL;
+  if (d->dtype != INKATTN_FP32 && d->dtype != INKATTN_BF16) return INKATTN_ENOTSUP;
+  if (d->head_dim != 128 || d->block_size != 128) return INKATTN_ENOTSUP;
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1) return INKATTN_EINVAL;
+  if (d->num_q_heads % d->num_kv_heads != 0) return INKATTN_EINVAL;
+  if (d->num_q_heads / d->num_kv_heads > 16) return INKATTN_ENOTSUP;
+  if (d->window < 0 || d->bias_len < 1) return INKATTN_EINVAL;
+  return INKATTN_OK;
+}
+
+AttnShape shape_of(const inkattn_attn_desc_t* d) {
+  return AttnShape{d->dtype, d->num_q_heads, d->num_kv_heads, d->window, d->bias_len};
+}
+
+// Number of 128-token blocks that the attended key range of the longest
+// sequence can touch.
+int64_t blocks_in_range(const inkattn_attn_desc_t* d, int64_t max_seq_len) {
+  const int64_t all = (max_seq_len + 127) / 128;
+  if (d->window == 0) return all;
+  const int64_t keys = d->window < max_seq_len ? d->window : max_seq_len;
+  const int64_t span = (keys + 127) / 128 + 1;   // +1: range need not be block aligned
+  return span < all ? span : all;
+}
+
+int32_t auto_splits(const inkattn_attn_desc_t* d, int32_t num_seqs, int32_t max_seq_len) {
+  const int64_t pairs = (int64_t)num_seqs * d->num_kv_heads;
+  const int64_t nblk = blocks_in_range(d, max_seq_len);
+  if (pairs <= 0 || nblk <= 0) return 1;
+  int64_t s = (kDecodeTargetGroups + pairs - 1) / pairs;
+  if (s > nblk) s = nblk;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
+inkattn_status_t from_hip(hipError_t e) { return e == hipSuccess ? INKATTN_OK : INKATTN_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* inkattn_status_string(int32_t status) {
+  switch (status) {
+    case INKATTN_OK: return "ok";
+    case INKATTN_EINVAL: return "invalid argument";
+    case INKATTN_ENOTSUP: return "unsupported configuration";
+    case INKATTN_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+inkattn_status_t inkattn_sconv(int32_t dtype, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t num_seqs, int32_t num_tokens, int32_t max_chunk_len,
+                               const void* k_in, const void* v_in, const void* conv_w,
+                               void* conv_state, const int32_t* state_slot,
+                               const int32_t* cu_seqlens, const int32_t* slot_mapping,
+                               void* k_cache, void* v_cache, void* stream) {
+  if (dtype != INKATTN_FP32 && dtype != INKATTN_BF16) return INKATTN_ENOTSUP;
+  if (head_dim != 128) return INKATTN_ENOTSUP;
+  if (num_kv_heads < 1) return INKATTN_EINVAL;
+  if (num_kv_heads > 64) return INKATTN_ENOTSUP;       // one thread per 8 channels, <= 1024
+  if (num_seqs < 0 || num_tokens < 0 || max_chunk_len < 0) return INKATTN_EINVAL;
+  if (num_seqs == 0 || num_tokens == 0 || max_chunk_len == 0) return INKATTN_OK;
+  if (!k_in || !v_in || !conv_w || !conv_state || !state_slot || !cu_seqlens ||
+      !slot_mapping || !k_cache || !v_cache)
+    return INKATTN_EINVAL;
+  if (!aligned16(k_in) || !aligned16(v_in) || !aligned16(conv_w) || !aligned16(conv_state) ||
+      !aligned16(k_cache) || !aligned16(v_cache))
+    return INKATTN_EINVAL;
+  return from_hip(inkattn::launch_sconv(dtype, num_kv_heads, num_seqs, max_chunk_len, k_in,
+                                        v_in, conv_w, conv_state, state_slot, cu_seqlens,
+                                        slot_mapping, k_cache, v_cache,
+                                        (hipStream_t)stream));
+}
+
+inkattn_status_t inkattn_relattn_prefill(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                         int32_t num_tokens, int32_t max_q_len,
+                                         const void* q, const void* k_cache,
+                                         const void* v_cache, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq,
+                                         const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                         const void* bias, void* out, float* lse,
+                                         void* stream) {
+  inkattn_status_t st = check_desc(desc);
+  if (st != INKATTN_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0) return INKATTN_EINVAL;
+  if (num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return INKATTN_OK;
+  if (max_blocks_per_seq < 1) return INKATTN_EINVAL;
+  if (!q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !seq_lens || !bias ||
+      !out)
+    return INKATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return INKATTN_EINVAL;
+  return from_hip(inkattn::launch_prefill(shape_of(desc), num_seqs, max_q_len, q, k_cache,
+                                          v_cache, block_table, max_blocks_per_seq,
+                                          cu_seqlens_q, seq_lens, bias, out, lse,
+                                          (hipStream_t)stream));
+}
+
+int32_t inkattn_relattn_decode_num_splits(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                          int32_t max_seq_len) {
+  if (check_desc(desc) != INKATTN_OK || num_seqs < 1 || max_seq_len < 1) return 1;
+  return auto_splits(desc, num_seqs, max_seq_len);
+}
+
+size_t inkattn_relattn_decode_workspace_size(const inkattn_attn_desc_t* desc,
+                                             int32_t num_seqs, int32_t max_seq_len,
+                                             int32_t num_splits) {
+  if (check_desc(desc) != INKATTN_OK || num_seqs < 0 || max_seq_len < 0 || num_splits < 0)
+    return 0;
+  const int64_t s = num_splits == 0 ? auto_splits(desc, num_seqs, max_seq_len) : num_splits;
+  const size_t rows = (size_t)num_seqs * desc->num_q_heads * (size_t)s;
+  return rows * 128 * sizeof(float) + ((rows * sizeof(float) + 15) & ~(size_t)15);
+}
+
+inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                        int32_t max_seq_len, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const int32_t* block_table,
+                                        int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                        const void* bias, void* out, float* lse,
+                                        int32_t num_splits, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  inkattn_status_t st = check_desc(desc);
+  if (st != INKATTN_OK) return st;
+  if (num_seqs < 0 || max_seq_len < 0 || num_splits < 0) return INKATTN_EINVAL;
+  if (num_seqs == 0) return INKATTN_OK;
+  if (max_seq_len < 1 || max_blocks_per_seq < 1) return INKATTN_EINVAL;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !bias || !out || !workspace)
+    return INKATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(workspace))
+    return INKATTN_EINVAL;
+  const int32_t s = num_splits == 0 ? auto_splits(desc, num_seqs, max_seq_len) : num_splits;
+  const size_t need = inkattn_relattn_decode_workspace_size(desc, num_seqs, max_seq_len, s);
+  if (workspace_bytes < need) return INKATTN_EINVAL;
+  const size_t rows = (size_t)num_seqs * desc->num_q_heads * (size_t)s;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = part_o + rows * 128;
+  return from_hip(inkattn::launch_decode(shape_of(desc), num_seqs, s, q, k_cache, v_cache,
+                                         block_table, max_blocks_per_seq, seq_lens, bias,
+                                         out, lse, part_o, part_lse, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,270 @@
+// Split-K paged decode for relative-position GQA attention, plus the
+// log-sum-exp merge of the splits.
+//
+// Source: news article "vLLM, TML Inkling Day-0 support", Model Architecture /
+// Attention (GQA, head size 128, sliding-window and full layers, a learned
+// relative-position term added to the logits) and vLLM Integration &
+// Optimization / FA4 with sheared bias (the KV range is cut into a
+// per-configuration number of splits).  Logit of query head h at position
+// L-1 against key j:  q.k_j / sqrt(128) + bias[h][min(L-1-j, R-1)].
+//
+// Split kernel: one work-group of 4 waves per (split, kv-head, sequence).
+// The split owns a contiguous run of 128-token pages of the sequence's key
+// range; in every page wave w takes keys 32w .. 32w+31 and reads them straight
+// from HBM into MFMA operand registers (16 B per lane per load, next page
+// prefetched while the current one is computed), so the kernel streams each
+// K/V byte of the range exactly once.  All Hq/Hkv query heads of the group
+// ride along in one 16-wide MFMA column tile:
+//   S^T[key][head] = K Q^T    (v_mfma 16x16x32, rows = keys, cols = heads)
+//   O^T[d][head]  += V^T P^T  (v_mfma 16x16x32, rows = dims,  cols = heads)
+// V is stored transposed per page (v_cache [block][kvh][d][token]) so that
+// the A operand of the second product is 8 consecutive tokens of one dim, a
+// contiguous 16 B load.  Rows of the first product are ordered so that lane
+// group G ends up holding the probabilities of keys 8G .. 8G+7, exactly the
+// B-operand layout of the second product (no shuffles).
+// The four waves merge their running (max, sum, O) through LDS and write one
+// normalised partial output and its log-sum-exp per (sequence, head, split).
+//
+// Merge kernel: per (sequence, q-head), lse = log sum_s exp(lse_s) and
+// out = sum_s exp(lse_s - lse) o_s; splits that saw no key have lse = -inf.
+#include "device_common.h"
+#include "launch.h"
+
+namespace inkattn {
+
+namespace {
+
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+
+template <typename T>
+__device__ __forceinline__ Frag8<T> zero_tail(const Frag8<T>& f, int nvalid) {
+  // keep elements e < nvalid, zero the rest
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = e < nvalid ? f.get(e) : 0.0f;
+  return Frag8<T>::pack(x);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
+    int Hq, int Hkv, int window, int R, int S, const T* __restrict__ q,
+    const T* __restrict__ k_cache, const T* __restrict__ v_cache,
+    const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seq_lens,
+    const T* __restrict__ bias, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ float sm_m[kDecodeWaves][16];
+  __shared__ float sm_l[kDecodeWaves][16];
+  __shared__ float sm_o[kDecodeWaves][16][kHeadDim + 4];
+
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;      // MFMA column (query head in group) / row index for A loads
+  const int grp = lane >> 4;      // lane group 0..3
+
+  const int L = seq_lens[b];
+  const int kstart = window > 0 ? max(0, L - window) : 0;
+  const int blk_first = kstart >> 7;
+  const int blk_last = (L - 1) >> 7;
+  const int nblk = blk_last - blk_first + 1;
+  const int bps = (nblk + S - 1) / S;
+  const int my_lo = blk_first + split * bps;
+  const int my_hi = min(my_lo + bps, blk_last + 1);
+
+  const bool head_ok = col < G;
+  const int h = kvh * G + col;
+  Frag8<T> qf[4];
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds)
+    qf[ds] = head_ok ? Frag8<T>::load(q + ((size_t)b * Hq + h) * kHeadDim + 32 * ds + 8 * grp)
+                     : Frag8<T>::zero();
+  const T* bias_h = bias + (size_t)(head_ok ? h : 0) * R;
+
+  const float c = 0.08838834764831845f * kLog2e;   // log2(e) / sqrt(128)
+  float m = -INFINITY;                             // running max (log2 units)
+  float l = 0.0f;                                  // this lane's share of the sum
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0, 0, 0, 0};
+
+  // Row r of the S^T tile t is key 32w + 8*(r/4) + 4t + r%4, so accumulator
+  // register r of lane group G in tile t holds key 32w + 8G + 4t + r.
+  const int krow_base = 32 * wave + 8 * (col >> 2) + (col & 3);
+  const int key_lane = 32 * wave + 8 * grp;   // first of this lane's 8 keys in the page
+
+  auto page_base = [&](int blk) -> size_t {
+    const int phys = block_table[(size_t)b * max_blocks + blk];
+    return ((size_t)phys * Hkv + kvh) * (size_t)(kPage * kHeadDim);
+  };
+  auto load_page = [&](int blk, Frag8<T>* kf, Frag8<T>* vf) {
+    const size_t base = page_base(blk);
+    const T* kt = k_cache + base;
+    const T* vt = v_cache + base;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds)
+        kf[t * 4 + ds] = Frag8<T>::load(kt + (size_t)(krow_base + 4 * t) * kHeadDim + 32 * ds + 8 * grp);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      vf[dt] = Frag8<T>::load(vt + (size_t)(16 * dt + col) * kPage + key_lane);
+  };
+
+  Frag8<T> kf[8], vf[8];
+  if (my_lo < my_hi) load_page(my_lo, kf, vf);
+  for (int blk = my_lo; blk < my_hi; ++blk) {
+    Frag8<T> kn[8], vn[8];
+    if (blk + 1 < my_hi) load_page(blk + 1, kn, vn);
+
+    // Relative bias of this lane's 8 keys (distance L-1-j, clipped to R-1).
+    const int j0 = blk * kPage + key_lane;
+    float bv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int dist = L - 1 - (j0 + e);
+      bv[e] = (head_ok && dist >= 0) ? to_f32(bias_h[min(dist, R - 1)]) * kLog2e : 0.0f;
+    }
+
+    f32x4 sacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sacc[t] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) sacc[t] = mfma16(kf[t * 4 + ds], qf[ds], sacc[t]);
+    }
+
+    float x[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + e;
+      const bool ok = head_ok && j >= kstart && j < L;
+      x[e] = ok ? sacc[e >> 2][e & 3] * c + bv[e] : -INFINITY;
+      mx = fmaxf(mx, x[e]);
+    }
+    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = fast_exp2(m - m_sub);       // m = -inf -> 0
+    float p[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = fast_exp2(x[e] - m_sub);
+      psum += p[e];
+    }
+    l = l * alpha + psum;
+    m = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+
+    const Frag8<T> pf = Frag8<T>::pack(p);
+    // Keys >= L of the last page hold no data (possibly NaN): zero them in V
+    // so that 0 * garbage cannot reach O.  The branch is wave-uniform; the
+    // per-lane part is a select, never a divergent branch around the MFMA
+    // (matrix instructions must run with every lane active).
+    if (blk == blk_last && (L & (kPage - 1)) != 0) {
+      const int nvalid = L - (blk * kPage + key_lane);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) vf[dt] = zero_tail(vf[dt], nvalid);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = mfma16(vf[dt], pf, o[dt]);
+
+    if (blk + 1 < my_hi) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { kf[i] = kn[i]; vf[i] = vn[i]; }
+    }
+  }
+
+  // Merge the four waves.  O^T register r of tile dt is dim 16dt + 4G + r.
+  float lt = l + wave_shfl_xor(l, 16);
+  lt += wave_shfl_xor(lt, 32);
+  if (grp == 0) {
+    sm_m[wave][col] = m;
+    sm_l[wave][col] = lt;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm_o[wave][col][16 * dt + 4 * grp + r] = o[dt][r];
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kDecodeThreads) {
+    const int hh = idx / kHeadDim;
+    const int d = idx % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm_m[w][hh]);
+    const size_t row = ((size_t)b * Hq + kvh * G + hh) * S + split;
+    if (M == -INFINITY) {
+      part_o[row * kHeadDim + d] = 0.0f;
+      if (d == 0) part_lse[row] = -INFINITY;
+      continue;
+    }
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float sc = fast_exp2(sm_m[w][hh] - M);
+      num += sc * sm_o[w][hh][d];
+      den += sc * sm_l[w][hh];
+    }
+    part_o[row * kHeadDim + d] = num / den;
+    if (d == 0) part_lse[row] = (M + fast_log2(den)) * kLn2;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(
+    int Hq, int S, const float* __restrict__ part_o, const float* __restrict__ part_lse,
+    T* __restrict__ out, float* __restrict__ lse) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int d = threadIdx.x;
+  const size_t row0 = ((size_t)b * Hq + h) * S;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, part_lse[row0 + s]);
+  float num = 0.0f, den = 0.0f;
+  for (int s = 0; s < S; ++s) {
+    const float ls = part_lse[row0 + s];
+    if (ls == -INFINITY) continue;
+    const float w = fast_exp2((ls - M) * kLog2e);
+    num += w * part_o[(row0 + s) * kHeadDim + d];
+    den += w;
+  }
+  out[((size_t)b * Hq + h) * kHeadDim + d] = from_f32<T>(num / den);
+  if (lse != nullptr && d == 0) lse[(size_t)b * Hq + h] = M + fast_log2(den) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_splits, const void* q,
+                         const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, int max_blocks_per_seq,
+                         const int32_t* seq_lens, const void* bias, void* out, float* lse,
+                         float* part_o, float* part_lse, hipStream_t stream) {
+  dim3 grid(num_splits, s.Hkv, num_seqs);
+  dim3 mgrid(s.Hq, num_seqs);
+  if (s.dtype == kDtypeBf16) {
+    hipLaunchKernelGGL(decode_split_kernel<bf16>, grid, dim3(kDecodeThreads), 0, stream, s.Hq,
+                       s.Hkv, s.window, s.bias_len, num_splits, (const bf16*)q,
+                       (const bf16*)k_cache, (const bf16*)v_cache, block_table,
+                       max_blocks_per_seq, seq_lens, (const bf16*)bias, part_o, part_lse);
+    hipLaunchKernelGGL(decode_merge_kernel<bf16>, mgrid, dim3(kHeadDim), 0, stream, s.Hq,
+                       num_splits, part_o, part_lse, (bf16*)out, lse);
+  } else {
+    hipLaunchKernelGGL(decode_split_kernel<float>, grid, dim3(kDecodeThreads), 0, stream, s.Hq,
+                       s.Hkv, s.window, s.bias_len, num_splits, (const float*)q,
+                       (const float*)k_cache, (const float*)v_cache, block_table,
+                       max_blocks_per_seq, seq_lens, (const float*)bias, part_o, part_lse);
+    hipLaunchKernelGGL(decode_merge_kernel<float>, mgrid, dim3(kHeadDim), 0, stream, s.Hq,
+                       num_splits, part_o, part_lse, (float*)out, lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace inkattn

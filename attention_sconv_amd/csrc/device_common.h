@@ -1,0 +1,136 @@
+// Device-side building blocks shared by the libinkattn kernels (gfx950 only).
+//
+// Element types: the library stores activations either as fp32 or as bf16
+// (bit pattern in a uint16_t).  Arithmetic is always fp32.
+//
+// MFMA fragments.  Every matrix-core call in this library contracts over a
+// run of k-values in which lane group G of the wave (G = lane/32 for the
+// 32x32 shapes, lane/16 for the 16x16 shapes) supplies 8 consecutive
+// k-values, 8G .. 8G+7, held as one "frag8" (8 elements of the storage type).
+//   bf16: one v_mfma_f32_32x32x16_bf16 / v_mfma_f32_16x16x32_bf16;
+//   fp32: eight v_mfma_f32_32x32x2_f32 / v_mfma_f32_16x16x4_f32, call e using
+//         element e of every lane (so lane group G again supplies k = 8G+e).
+// Both contract exactly the same (a, b) pairs, so one kernel template serves
+// both storage types.
+//
+// Accumulator layouts (CDNA3/CDNA4 matrix cores):
+//   32x32: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+//   16x16: lane l, register r holds row 4*(l/16) + r, column l%16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace inkattn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct bf16 { uint16_t bits; };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kHeadDim = 128;
+constexpr int kPage = 128;          // KV-cache block (tokens per page)
+
+// ---------------------------------------------------------------- scalars
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) {
+  return __uint_as_float(uint32_t(x.bits) << 16);
+}
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
+  return bf16{f32_to_bf16_bits(x)};
+}
+
+// ---------------------------------------------------------------- frag8
+template <typename T> struct Frag8;
+
+template <> struct Frag8<bf16> {
+  u32x4 v;                                   // 8 bf16, element e in bits 16*(e%2) of word e/2
+  __device__ __forceinline__ static Frag8 load(const bf16* p) {
+    Frag8 f; f.v = *reinterpret_cast<const u32x4*>(p); return f;
+  }
+  __device__ __forceinline__ void store(bf16* p) const {
+    *reinterpret_cast<u32x4*>(p) = v;
+  }
+  __device__ __forceinline__ static Frag8 zero() { Frag8 f; f.v = u32x4{0, 0, 0, 0}; return f; }
+  __device__ __forceinline__ float get(int e) const {
+    uint32_t w = v[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  // Pack 8 fp32 values (round to nearest even).
+  __device__ __forceinline__ static Frag8 pack(const float* x) {
+    Frag8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.v[i] = uint32_t(f32_to_bf16_bits(x[2 * i])) |
+               (uint32_t(f32_to_bf16_bits(x[2 * i + 1])) << 16);
+    return f;
+  }
+  __device__ __forceinline__ bf16x8_t as_mfma() const {
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+};
+
+template <> struct Frag8<float> {
+  f32x4 lo, hi;
+  __device__ __forceinline__ static Frag8 load(const float* p) {
+    Frag8 f;
+    f.lo = *reinterpret_cast<const f32x4*>(p);
+    f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+    return f;
+  }
+  __device__ __forceinline__ void store(float* p) const {
+    *reinterpret_cast<f32x4*>(p) = lo;
+    *reinterpret_cast<f32x4*>(p + 4) = hi;
+  }
+  __device__ __forceinline__ static Frag8 zero() {
+    Frag8 f; f.lo = f32x4{0, 0, 0, 0}; f.hi = f.lo; return f;
+  }
+  __device__ __forceinline__ float get(int e) const { return e < 4 ? lo[e] : hi[e - 4]; }
+  __device__ __forceinline__ static Frag8 pack(const float* x) {
+    Frag8 f;
+    f.lo = f32x4{x[0], x[1], x[2], x[3]};
+    f.hi = f32x4{x[4], x[5], x[6], x[7]};
+    return f;
+  }
+};
+
+// 32x32 output, contracts 16 k-values (lane group lane/32 holds k = 8G..8G+7).
+__device__ __forceinline__ f32x16 mfma32(const Frag8<bf16>& a, const Frag8<bf16>& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.as_mfma(), b.as_mfma(), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const Frag8<float>& a, const Frag8<float>& b, f32x16 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.get(e), b.get(e), c, 0, 0, 0);
+  return c;
+}
+// 16x16 output, contracts 32 k-values (lane group lane/16 holds k = 8G..8G+7).
+__device__ __forceinline__ f32x4 mfma16(const Frag8<bf16>& a, const Frag8<bf16>& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.as_mfma(), b.as_mfma(), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const Frag8<float>& a, const Frag8<float>& b, f32x4 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.get(e), b.get(e), c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float wave_shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace inkattn

@@ -1,0 +1,36 @@
+// Internal launcher interface between the C-ABI layer (api.hip) and the
+// kernel translation units.  Arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace inkattn {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBf16 = 1;
+
+hipError_t launch_sconv(int dtype, int Hkv, int num_seqs, int max_chunk_len,
+                        const void* k_in, const void* v_in, const void* conv_w,
+                        void* conv_state, const int32_t* state_slot,
+                        const int32_t* cu_seqlens, const int32_t* slot_mapping,
+                        void* k_cache, void* v_cache, hipStream_t stream);
+
+struct AttnShape {
+  int dtype, Hq, Hkv, window, bias_len;
+};
+
+hipError_t launch_prefill(const AttnShape& s, int num_seqs, int max_q_len, const void* q,
+                          const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                          const void* bias, void* out, float* lse, hipStream_t stream);
+
+hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_splits, const void* q,
+                         const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, int max_blocks_per_seq,
+                         const int32_t* seq_lens, const void* bias, void* out, float* lse,
+                         float* part_o, float* part_lse, hipStream_t stream);
+
+}  // namespace inkattn

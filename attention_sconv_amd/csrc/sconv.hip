@@ -1,0 +1,130 @@
+// Short convolution (window 4, causal, depthwise) of keys and values, fused
+// with the write into the paged KV cache and the update of the three-token
+// state cache.
+//
+// Source: news article "vLLM, TML Inkling Day-0 support", Model Architecture /
+// Sconv (window-4 short convolution over the attention key and value
+// channels) and vLLM Integration & Optimization / Managing the sconv cache
+// (the last W-1 tokens are kept).  The cached rows are the pre-convolution
+// inputs; tap 3 weights the current token.
+//
+// Work split: grid (token chunk, sequence, K|V); each thread owns 8
+// consecutive channels (one 16-byte bf16 vector, two for fp32), so a wave
+// reads a 1 KiB channel-contiguous row per token (Hkv = 4), and walks up to
+// kChunk tokens of one sequence with the last three inputs held in
+// registers.  Only the thread that handles a sequence's first chunk touches
+// that sequence's state, so the in-place state update is race-free.
+// Memory-bound: every input byte is read once (plus a 3-row halo per chunk)
+// and every output byte written once.
+#include "device_common.h"
+#include "launch.h"
+
+namespace inkattn {
+
+constexpr int kSconvChunk = 16;
+
+template <typename T>
+__global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
+    int C, int Hkv, const T* __restrict__ k_in, const T* __restrict__ v_in,
+    const T* __restrict__ conv_w, T* __restrict__ conv_state,
+    const int32_t* __restrict__ state_slot, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ slot_mapping, T* __restrict__ k_cache,
+    T* __restrict__ v_cache) {
+  const int which = blockIdx.z;              // 0 = keys, 1 = values
+  const int b = blockIdx.y;
+  const int r0 = blockIdx.x * kSconvChunk;   // first token of the chunk (relative)
+  const int c0 = threadIdx.x * 8;
+  const int t_begin = cu_seqlens[b];
+  const int n = cu_seqlens[b + 1] - t_begin;
+  if (r0 >= n) return;
+
+  const T* x = (which ? v_in : k_in) + (size_t)t_begin * C + c0;
+  const T* wp = conv_w + ((size_t)which * C + c0) * 4;
+  T* st = conv_state + ((size_t)state_slot[b] * 2 + which) * 3 * C + c0;
+
+  float w[8][4];
+  {
+    Frag8<T> f0 = Frag8<T>::load(wp), f1 = Frag8<T>::load(wp + 8),
+             f2 = Frag8<T>::load(wp + 16), f3 = Frag8<T>::load(wp + 24);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const Frag8<T>& f = e < 2 ? f0 : e < 4 ? f1 : e < 6 ? f2 : f3;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[e][k] = f.get((e & 1) * 4 + k);
+    }
+  }
+
+  // Inputs of the three tokens before r0: from this chunk's sequence, or
+  // from the cached state for positions before the chunk start.
+  Frag8<T> h0, h1, h2;
+  {
+    Frag8<T> hk[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int rel = r0 - 3 + k;
+      hk[k] = rel >= 0 ? Frag8<T>::load(x + (size_t)rel * C)
+                       : Frag8<T>::load(st + (size_t)(rel + 3) * C);
+    }
+    h0 = hk[0]; h1 = hk[1]; h2 = hk[2];
+  }
+
+  const int kvh = c0 / kHeadDim;
+  const int dd = c0 % kHeadDim;
+  const int r_end = min(r0 + kSconvChunk, n);
+  for (int r = r0; r < r_end; ++r) {
+    const Frag8<T> cur = Frag8<T>::load(x + (size_t)r * C);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      y[e] = w[e][0] * h0.get(e) + w[e][1] * h1.get(e) + w[e][2] * h2.get(e) +
+             w[e][3] * cur.get(e);
+    const int slot = slot_mapping[t_begin + r];
+    const size_t tile = (size_t)(slot >> 7) * Hkv + kvh;
+    const int off = slot & (kPage - 1);
+    if (which == 0) {
+      Frag8<T>::pack(y).store(k_cache + (tile * kPage + off) * kHeadDim + dd);
+    } else {
+      T* vt = v_cache + (tile * kHeadDim + dd) * kPage + off;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[(size_t)e * kPage] = from_f32<T>(y[e]);
+    }
+    h0 = h1; h1 = h2; h2 = cur;
+  }
+
+  if (r0 == 0) {
+    // New state = last three rows of [old state; chunk inputs].
+    Frag8<T> ns[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int rel = n - 3 + k;
+      ns[k] = rel >= 0 ? Frag8<T>::load(x + (size_t)rel * C)
+                       : Frag8<T>::load(st + (size_t)(rel + 3) * C);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) ns[k].store(st + (size_t)k * C);
+  }
+}
+
+hipError_t launch_sconv(int dtype, int Hkv, int num_seqs, int max_chunk_len,
+                        const void* k_in, const void* v_in, const void* conv_w,
+                        void* conv_state, const int32_t* state_slot,
+                        const int32_t* cu_seqlens, const int32_t* slot_mapping,
+                        void* k_cache, void* v_cache, hipStream_t stream) {
+  const int C = Hkv * kHeadDim;
+  dim3 grid((max_chunk_len + kSconvChunk - 1) / kSconvChunk, num_seqs, 2);
+  dim3 block(C / 8);
+  if (dtype == kDtypeBf16) {
+    hipLaunchKernelGGL(sconv_cache_write_kernel<bf16>, grid, block, 0, stream, C, Hkv,
+                       (const bf16*)k_in, (const bf16*)v_in, (const bf16*)conv_w,
+                       (bf16*)conv_state, state_slot, cu_seqlens, slot_mapping,
+                       (bf16*)k_cache, (bf16*)v_cache);
+  } else {
+    hipLaunchKernelGGL(sconv_cache_write_kernel<float>, grid, block, 0, stream, C, Hkv,
+                       (const float*)k_in, (const float*)v_in, (const float*)conv_w,
+                       (float*)conv_state, state_slot, cu_seqlens, slot_mapping,
+                       (float*)k_cache, (float*)v_cache);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace inkattn

@@ -1,0 +1,174 @@
+/*
+ * libinkattn -- the Inkling attention-block hot path on AMD Instinct MI355X
+ * (gfx950): short convolution of keys and values fused into the paged
+ * KV-cache write, and relative-position grouped-query attention (prefill and
+ * split-K decode).
+ *
+ * Sources (web pages this library is built from):
+ *   [A] news article "vLLM, TML Inkling Day-0 support" (news.ainew.jp),
+ *       sections Model Architecture / Attention, Model Architecture / Sconv,
+ *       vLLM Integration & Optimization / Managing the sconv cache and
+ *       / FA4 with sheared bias;
+ *   [B] vLLM recipe "thinkingmachines/Inkling", Guide / Overview and
+ *       Client Usage (MI355X launch with a KV block size of 128);
+ *   [C] vLLM recipe "thinkingmachines/Inkling-Small", Client Usage (same).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All array arguments are DEVICE pointers into memory the caller owns.
+ *   The library never allocates, frees or synchronises; every launch is
+ *   asynchronous on `stream` (a hipStream_t passed as void*, NULL = the null
+ *   stream).  The library keeps no global state and is thread-safe.
+ * - Scalar arguments (counts, maxima) are host values.
+ * - Storage dtype INKATTN_FP32 (float) or INKATTN_BF16 (bfloat16 bits);
+ *   all arithmetic is fp32.  q, K/V, conv weights/state, bias and out share
+ *   the dtype; lse and the decode workspace are always float.
+ * - head_dim must be 128 and the KV block (page) 128 tokens ([A] Attention;
+ *   [B], [C] MI355X launch).
+ * - KV-cache layout, one 32 KiB (bf16) tile per (block, kv-head):
+ *       k_cache [num_blocks][num_kv_heads][128 tokens][128 dims]
+ *       v_cache [num_blocks][num_kv_heads][128 dims][128 tokens]   (V^T)
+ *   Token position p of sequence b is slot
+ *       block_table[b][p / 128] * 128 + p % 128.
+ * - Device-side preconditions are not checked (that would need a sync):
+ *   indices in range, distinct state slots per call, every cache entry of
+ *   positions < seq_len finite, 1 <= q_len <= seq_len.
+ * - Errors: host-side checks run before any launch.  INKATTN_EINVAL for a
+ *   NULL required pointer, a bad size or a misaligned pointer (16 B);
+ *   INKATTN_ENOTSUP for an unsupported dtype, head_dim, block size or GQA
+ *   group; INKATTN_EHIP when the HIP runtime reports a launch failure.
+ *   Nothing aborts and no exception crosses the ABI.
+ */
+#ifndef INKATTN_H_
+#define INKATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  INKATTN_OK = 0,
+  INKATTN_EINVAL = 1,
+  INKATTN_ENOTSUP = 2,
+  INKATTN_EHIP = 3
+} inkattn_status_t;
+
+typedef enum { INKATTN_FP32 = 0, INKATTN_BF16 = 1 } inkattn_dtype_t;
+
+/* Attention layer description.
+ *   window   : sliding window W (query i sees keys j with 0 <= i-j <= W-1);
+ *              0 = full causal ([A] Attention: sliding-window and full layers).
+ *   bias_len : R >= 1, length of each row of the relative-position table;
+ *              distances >= R use entry R-1. */
+typedef struct {
+  int32_t dtype;          /* inkattn_dtype_t */
+  int32_t num_q_heads;    /* Hq */
+  int32_t num_kv_heads;   /* Hkv; Hq % Hkv == 0, Hq/Hkv <= 16 */
+  int32_t head_dim;       /* must be 128 */
+  int32_t block_size;     /* must be 128 */
+  int32_t window;         /* W >= 0 */
+  int32_t bias_len;       /* R >= 1 */
+} inkattn_attn_desc_t;
+
+/* Short convolution of keys and values, fused with the paged KV-cache write
+ * ([A] Sconv: window-4 convolution over key and value channels;
+ *  [A] Managing the sconv cache: the last W-1 = 3 tokens are cached).
+ *
+ * For each sequence b (tokens cu_seqlens[b] .. cu_seqlens[b+1]-1) and each
+ * channel c of K (and separately of V):
+ *   xp = [conv_state[state_slot[b]][which][0..2][c]; x[tokens][c]]
+ *   y[t][c] = sum_{k=0..3} conv_w[which][c][k] * xp[t+k][c]
+ *   (tap 3 weights the current token), y is rounded to dtype and written to
+ *   the cache slot slot_mapping[t]; afterwards conv_state[state_slot[b]][which]
+ *   holds the last 3 rows of xp (pre-convolution values).  A fresh sequence
+ *   passes a zeroed state.
+ *
+ *   k_in, v_in   [num_tokens][Hkv*128]      pre-convolution keys / values
+ *   conv_w       [2][Hkv*128][4]            [0] keys, [1] values
+ *   conv_state   [num_slots][2][3][Hkv*128] read, then updated in place
+ *   state_slot   int32 [num_seqs]           distinct within one call
+ *   cu_seqlens   int32 [num_seqs+1]
+ *   slot_mapping int32 [num_tokens]
+ *   k_cache, v_cache                        layouts above
+ *   max_chunk_len: host upper bound of cu_seqlens[b+1]-cu_seqlens[b].
+ * num_tokens == 0 or num_seqs == 0 is a no-op returning INKATTN_OK. */
+inkattn_status_t inkattn_sconv(int32_t dtype, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t num_seqs, int32_t num_tokens, int32_t max_chunk_len,
+                               const void* k_in, const void* v_in, const void* conv_w,
+                               void* conv_state, const int32_t* state_slot,
+                               const int32_t* cu_seqlens, const int32_t* slot_mapping,
+                               void* k_cache, void* v_cache, void* stream);
+
+/* Relative-position GQA attention over a chunk of new tokens per sequence
+ * ([A] Attention; [A] FA4 with sheared bias):
+ *   logit[h,i,j] = q_i . k_j / sqrt(128) + bias[h][min(i-j, R-1)]
+ * over keys j <= i (and i-j <= W-1 when W > 0), softmax, times V.  Query
+ * head h reads KV head h / (Hq/Hkv).  The chunk of sequence b
+ * (tokens cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1, q_len = their count)
+ * occupies positions seq_lens[b]-q_len .. seq_lens[b]-1; its keys and values
+ * must already be in the cache (inkattn_sconv).
+ *
+ *   q     [num_tokens][Hq][128]
+ *   block_table int32 [num_seqs][max_blocks_per_seq]
+ *   cu_seqlens_q int32 [num_seqs+1], seq_lens int32 [num_seqs]
+ *   bias  [Hq][R]
+ *   out   [num_tokens][Hq][128]
+ *   lse   float [num_tokens][Hq] = log(sum_j exp(logit_j)), or NULL
+ *   max_q_len: host upper bound of the per-sequence q_len. */
+inkattn_status_t inkattn_relattn_prefill(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                         int32_t num_tokens, int32_t max_q_len,
+                                         const void* q, const void* k_cache,
+                                         const void* v_cache, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq,
+                                         const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                         const void* bias, void* out, float* lse,
+                                         void* stream);
+
+/* Number of KV splits inkattn_relattn_decode uses for num_splits = 0 (auto):
+ * enough (sequence, kv-head, split) work-groups to fill the GPU, never more
+ * splits than 128-token blocks in the attended range ([A] FA4 with sheared
+ * bias: the split count is chosen from batch size and KV length). */
+int32_t inkattn_relattn_decode_num_splits(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                          int32_t max_seq_len);
+
+/* Workspace bytes inkattn_relattn_decode needs for this shape and split
+ * count (0 = auto): per (sequence, q-head, split) 128 floats of partial
+ * output plus one float of log-sum-exp.  Returns 0 for an invalid desc. */
+size_t inkattn_relattn_decode_workspace_size(const inkattn_attn_desc_t* desc,
+                                             int32_t num_seqs, int32_t max_seq_len,
+                                             int32_t num_splits);
+
+/* One decode step: the query of each sequence sits at position
+ * seq_lens[b]-1, whose key and value are already in the cache
+ * (inkattn_sconv with one token per sequence, same stream, earlier).
+ * Same logits as inkattn_relattn_prefill.  Split-K: each (sequence, kv-head,
+ * split) work-group attends over its share of the key blocks with all
+ * Hq/Hkv query heads of the group, writes a partial output and
+ * log-sum-exp to `workspace`, and a second kernel merges the splits.
+ *
+ *   q     [num_seqs][Hq][128]
+ *   out   [num_seqs][Hq][128], lse float [num_seqs][Hq] or NULL
+ *   max_seq_len: host upper bound of seq_lens[b].
+ *   num_splits : 0 = auto (inkattn_relattn_decode_num_splits), else >= 1.
+ *   workspace  : device memory of at least
+ *                inkattn_relattn_decode_workspace_size(...) bytes, 16 B aligned. */
+inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                        int32_t max_seq_len, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const int32_t* block_table,
+                                        int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                        const void* bias, void* out, float* lse,
+                                        int32_t num_splits, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* inkattn_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INKATTN_H_ */

@@ -80,11 +80,11 @@ def relattn_rows(q_rows, positions, K, V, bias, window, num_q_heads_per_kv,
         dist = np.minimum(i - j, R - 1)
         for h in range(Hq):
             g = h // num_q_heads_per_kv
-            s = (K[j, g, :] @ q_rows[r, h]) * scale + bias[h, dist]
+            s = (K[lo:hi + 1, g, :] @ q_rows[r, h]) * scale + bias[h, dist]
             m = s.max()
             e = np.exp(s - m)
             den = e.sum()
-            out[r, h] = (e @ V[j, g, :]) / den
+            out[r, h] = (e @ V[lo:hi + 1, g, :]) / den
             lse[r, h] = m + math.log(den)
     return out, lse
 

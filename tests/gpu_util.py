@@ -1,0 +1,161 @@
+"""Host-side helpers for the GPU parity tests: move a ``synth`` case to the
+device, call the library through its C ABI, and build the oracle's view of
+the same inputs.  No attention arithmetic here: expected values come from
+``oracle`` only."""
+
+import numpy as np
+import torch
+
+import attention_sconv_amd as ink
+from attention_sconv_amd import kvcache
+import oracle
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+def tdtype(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def ddtype(dtype):
+    return ink.BF16 if dtype == "bf16" else ink.FP32
+
+
+def dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(tdtype(dtype))
+
+
+def idev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda")
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+class GpuCase:
+    """Device copies of a synth.Case plus a KV cache in the library layout.
+    Cache slots that no token has written hold NaN, so any read of them shows."""
+
+    def __init__(self, case, fill_nan=True):
+        self.case = c = case
+        self.dt = c.dtype
+        self.q = dev(c.q, c.dtype)
+        self.k_pre = dev(c.k_pre, c.dtype)
+        self.v_pre = dev(c.v_pre, c.dtype)
+        self.conv_w = dev(c.conv_w, c.dtype)
+        self.conv_state = dev(c.conv_state, c.dtype)
+        self.state_slot = idev(c.state_slot)
+        self.cu = idev(c.cu_seqlens)
+        self.slot_mapping = idev(c.slot_mapping)
+        self.block_table = idev(c.block_table)
+        self.seq_lens = idev(c.seq_lens)
+        self.bias = dev(c.bias, c.dtype)
+        if c.past_k is not None:
+            pk = c.past_k if torch.is_tensor(c.past_k) else dev(c.past_k, c.dtype)
+            pv = c.past_v if torch.is_tensor(c.past_v) else dev(c.past_v, c.dtype)
+            self.k_cache, self.v_cache = kvcache.from_slots(pk, pv)
+            if fill_nan:
+                # slots beyond each sequence's context are unwritten
+                self._nan_unwritten()
+        else:
+            self.k_cache, self.v_cache = kvcache.alloc(c.num_blocks, c.num_kv_heads, c.dtype)
+            if fill_nan:
+                self.k_cache.fill_(float("nan"))
+                self.v_cache.fill_(float("nan"))
+            else:
+                self.k_cache.zero_()
+                self.v_cache.zero_()
+
+    def _nan_unwritten(self):
+        c = self.case
+        written = np.zeros(c.num_blocks * 128, dtype=bool)
+        for b in range(len(c.seq_lens)):
+            pos = np.arange(int(c.ctx_lens[b]))
+            written[oracle.slots_for(c.block_table[b], pos)] = True
+        bad = torch.from_numpy(np.nonzero(~written)[0]).to("cuda")
+        blk, off = bad // 128, bad % 128
+        self.k_cache[blk, :, off, :] = float("nan")
+        self.v_cache[blk, :, :, off] = float("nan")
+
+    # ---- library calls (through the C ABI) ----
+    def sconv(self, stream=None):
+        c = self.case
+        ink.inkattn_sconv(ddtype(self.dt), c.num_kv_heads, 128, len(c.q_lens), c.num_tokens,
+                          int(c.q_lens.max()), self.k_pre, self.v_pre, self.conv_w,
+                          self.conv_state, self.state_slot, self.cu, self.slot_mapping,
+                          self.k_cache, self.v_cache, stream)
+
+    def desc(self):
+        c = self.case
+        return ink.make_desc(ddtype(self.dt), c.num_q_heads, c.num_kv_heads, c.window,
+                             c.bias_len)
+
+    def prefill(self, with_lse=True, stream=None):
+        c = self.case
+        out = torch.empty_like(self.q)
+        lse = (torch.empty((c.num_tokens, c.num_q_heads), dtype=torch.float32, device="cuda")
+               if with_lse else None)
+        ink.inkattn_relattn_prefill(self.desc(), len(c.q_lens), c.num_tokens,
+                                    int(c.q_lens.max()), self.q, self.k_cache, self.v_cache,
+                                    self.block_table, self.block_table.shape[1], self.cu,
+                                    self.seq_lens, self.bias, out, lse, stream)
+        return out, lse
+
+    def decode(self, num_splits=0, with_lse=True, stream=None):
+        c = self.case
+        assert (c.q_lens == 1).all()
+        B = len(c.q_lens)
+        d = self.desc()
+        L = int(c.seq_lens.max())
+        ws_bytes = ink.inkattn_relattn_decode_workspace_size(d, B, L, num_splits)
+        ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
+        out = torch.empty_like(self.q)
+        lse = (torch.empty((B, c.num_q_heads), dtype=torch.float32, device="cuda")
+               if with_lse else None)
+        ink.inkattn_relattn_decode(d, B, L, self.q, self.k_cache, self.v_cache,
+                                   self.block_table, self.block_table.shape[1], self.seq_lens,
+                                   self.bias, out, lse, num_splits, ws, ws_bytes, stream)
+        return out, lse
+
+
+# ---- oracle side ----
+def oracle_sconv(case):
+    return oracle.sconv_batch(case.k_pre, case.v_pre, case.conv_w, case.conv_state,
+                              case.state_slot, case.cu_seqlens)
+
+
+def oracle_kv(case, b, k_new, v_new, lo=0):
+    """Logical K, V [L, Hkv, d] (float64) of sequence b: cached context from
+    the synth draw, then the oracle's post-convolution rows of the new tokens.
+    Positions below ``lo`` (outside every query's window) are left at zero."""
+    c = case
+    H, d = c.num_kv_heads, 128
+    ctx, L = int(c.ctx_lens[b]), int(c.seq_lens[b])
+    K = np.zeros((L, H, d))
+    V = np.zeros((L, H, d))
+    if ctx > lo:
+        slots = oracle.slots_for(c.block_table[b], np.arange(lo, ctx))
+        pk, pv = c.past_k, c.past_v
+        if torch.is_tensor(pk):
+            idx = torch.from_numpy(slots).to(pk.device)
+            K[lo:ctx] = pk[idx].float().cpu().numpy()
+            V[lo:ctx] = pv[idx].float().cpu().numpy()
+        else:
+            K[lo:ctx] = pk[slots]
+            V[lo:ctx] = pv[slots]
+    t0, t1 = int(c.cu_seqlens[b]), int(c.cu_seqlens[b + 1])
+    K[ctx:] = k_new[t0:t1].reshape(-1, H, d)
+    V[ctx:] = v_new[t0:t1].reshape(-1, H, d)
+    return K, V
+
+
+def assert_close(got, want, tol, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    err = np.abs(got - want)
+    i = np.unravel_index(np.argmax(err), err.shape)
+    assert err[i] <= tol, f"{what}: max-abs err {err[i]:.3e} at {i} > {tol} (got {got[i]}, want {want[i]})"
+    return float(err.max())

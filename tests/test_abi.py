@@ -1,0 +1,140 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/inkattn.h declares, and rejects bad arguments on the host before any
+HIP call.  No kernel is launched here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "inkattn.h")
+
+ink = pytest.importorskip("attention_sconv_amd")
+
+FAKE = 0x100000          # aligned non-NULL pointer; never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(inkattn_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(ink.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ink.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert ink.status_string(0) == "ok"
+    assert "invalid" in ink.status_string(1)
+    assert "unsupported" in ink.status_string(2)
+    assert "HIP" in ink.status_string(3)
+    assert ink.status_string(99) == "unknown status"
+
+
+def _sconv(**kw):
+    args = dict(dtype=1, Hkv=4, d=128, seqs=1, toks=4, maxc=4, k=FAKE, v=FAKE, w=FAKE,
+                st=FAKE, slot=FAKE, cu=FAKE, sm=FAKE, kc=FAKE, vc=FAKE)
+    args.update(kw)
+    return ink._lib._lib.inkattn_sconv(args["dtype"], args["Hkv"], args["d"], args["seqs"],
+                                       args["toks"], args["maxc"], args["k"], args["v"],
+                                       args["w"], args["st"], args["slot"], args["cu"],
+                                       args["sm"], args["kc"], args["vc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), ink.ENOTSUP), (dict(d=64), ink.ENOTSUP), (dict(Hkv=0), ink.EINVAL),
+    (dict(Hkv=65), ink.ENOTSUP), (dict(toks=-1), ink.EINVAL), (dict(k=None), ink.EINVAL),
+    (dict(kc=None), ink.EINVAL), (dict(k=FAKE + 8), ink.EINVAL),
+    (dict(toks=0), ink.OK), (dict(seqs=0), ink.OK),
+])
+def test_sconv_host_validation(kw, status):
+    assert _sconv(**kw) == status
+
+
+def _desc(**kw):
+    a = dict(dtype=1, Hq=32, Hkv=4, d=128, bs=128, W=0, R=64)
+    a.update(kw)
+    return ink.AttnDesc(a["dtype"], a["Hq"], a["Hkv"], a["d"], a["bs"], a["W"], a["R"])
+
+
+BAD_DESCS = [
+    (dict(dtype=2), ink.ENOTSUP), (dict(d=64), ink.ENOTSUP), (dict(bs=16), ink.ENOTSUP),
+    (dict(Hq=30), ink.EINVAL), (dict(Hkv=0), ink.EINVAL), (dict(W=-1), ink.EINVAL),
+    (dict(R=0), ink.EINVAL), (dict(Hq=64, Hkv=2), ink.ENOTSUP),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_DESCS)
+def test_prefill_rejects_bad_desc(kw, status):
+    lib = ink._lib._lib
+    d = _desc(**kw)
+    st = lib.inkattn_relattn_prefill(ctypes.byref(d), 1, 8, 8, FAKE, FAKE, FAKE, FAKE, 1,
+                                     FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == status
+
+
+def test_prefill_rejects_null_and_misaligned():
+    lib = ink._lib._lib
+    d = _desc()
+    assert lib.inkattn_relattn_prefill(None, 1, 8, 8, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE,
+                                       FAKE, FAKE, None, None) == ink.EINVAL
+    assert lib.inkattn_relattn_prefill(ctypes.byref(d), 1, 8, 8, None, FAKE, FAKE, FAKE, 1,
+                                       FAKE, FAKE, FAKE, FAKE, None, None) == ink.EINVAL
+    assert lib.inkattn_relattn_prefill(ctypes.byref(d), 1, 8, 8, FAKE + 2, FAKE, FAKE, FAKE,
+                                       1, FAKE, FAKE, FAKE, FAKE, None, None) == ink.EINVAL
+    assert lib.inkattn_relattn_prefill(ctypes.byref(d), 1, 8, 8, FAKE, FAKE, FAKE, FAKE, 0,
+                                       FAKE, FAKE, FAKE, FAKE, None, None) == ink.EINVAL
+    # empty work is a no-op, even with NULL pointers
+    assert lib.inkattn_relattn_prefill(ctypes.byref(d), 0, 0, 0, None, None, None, None, 1,
+                                       None, None, None, None, None, None) == ink.OK
+
+
+@pytest.mark.parametrize("kw,status", BAD_DESCS)
+def test_decode_rejects_bad_desc(kw, status):
+    lib = ink._lib._lib
+    d = _desc(**kw)
+    st = lib.inkattn_relattn_decode(ctypes.byref(d), 1, 100, FAKE, FAKE, FAKE, FAKE, 1, FAKE,
+                                    FAKE, FAKE, None, 0, FAKE, 1 << 30, None)
+    assert st == status
+    assert ink.inkattn_relattn_decode_workspace_size(d, 1, 100, 0) == 0
+
+
+def test_decode_workspace_rules():
+    d = _desc(W=4096, R=4096)
+    B, L = 64, 16384
+    s = ink.inkattn_relattn_decode_num_splits(d, B, L)
+    need = ink.inkattn_relattn_decode_workspace_size(d, B, L, 0)
+    rows = B * 32 * s
+    assert need == rows * 128 * 4 + ((rows * 4 + 15) // 16) * 16
+    assert ink.inkattn_relattn_decode_workspace_size(d, B, L, 3) == \
+        B * 32 * 3 * 128 * 4 + ((B * 32 * 3 * 4 + 15) // 16) * 16
+    lib = ink._lib._lib
+    st = lib.inkattn_relattn_decode(ctypes.byref(d), B, L, FAKE, FAKE, FAKE, FAKE, 128, FAKE,
+                                    FAKE, FAKE, None, 0, FAKE, need - 16, None)
+    assert st == ink.EINVAL
+    st = lib.inkattn_relattn_decode(ctypes.byref(d), B, L, FAKE, FAKE, FAKE, FAKE, 128, FAKE,
+                                    FAKE, FAKE, None, -1, FAKE, need, None)
+    assert st == ink.EINVAL
+    st = lib.inkattn_relattn_decode(ctypes.byref(d), B, L, FAKE, FAKE, FAKE, FAKE, 128, FAKE,
+                                    FAKE, FAKE, None, 0, FAKE + 4, need, None)
+    assert st == ink.EINVAL
+
+
+def test_num_splits_heuristic():
+    # enough (seq, kv-head, split) groups for 4 per compute unit, never more
+    # splits than pages in the attended range
+    sw = _desc(W=4096, R=4096)
+    assert ink.inkattn_relattn_decode_num_splits(sw, 64, 16384) == 4
+    full = _desc(W=0, R=1 << 20)
+    assert ink.inkattn_relattn_decode_num_splits(full, 4, 1 << 20) == 64
+    assert ink.inkattn_relattn_decode_num_splits(full, 1, 100) == 1
+    assert ink.inkattn_relattn_decode_num_splits(full, 1, 300) == 3
