@@ -245,12 +245,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
     const float m_tile = mx * c;
     const bool need = m_tile > m_used + kRescaleSlack;
     if (__any(need)) {
-      const float m_new = need ? m_tile : m_used;
-      const float alpha = fast_exp2(m_used - m_new);      // -inf -> 0, equal -> 1
+      // Lanes that do not need it keep their max (alpha = 1); this also keeps
+      // rows that have seen no key yet (m_used = -inf) free of -inf - -inf.
+      const float alpha = need ? fast_exp2(m_used - m_tile) : 1.0f;   // -inf -> 0
       l_sum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-      m_used = m_new;
+      m_used = need ? m_tile : m_used;
     }
     const float msub = m_used == -INFINITY ? 0.0f : m_used;
     Frag8<T> pf[4];

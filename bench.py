@@ -1,0 +1,262 @@
+"""Benchmark of the Inkling attention-block hot path on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input:
+  inkattn_sconv            (K/V short convolution + paged KV-cache write)
+  inkattn_relattn_prefill  (relative-position GQA attention over the chunk)
+on the sliding-window prefill workload (batch 1, T=8192, Hq=32, Hkv=4,
+d=128, window 2048, R=2048, bf16, paged KV block 128).  The decode half of
+the metric (split-K decode + LSE merge, after the one-token sconv) is measured
+in the same run on the 16K sliding-window decode workload (batch 64,
+L=16384, window 4096) and reported under "decode".
+
+Prints ONE JSON line.  value = algorithmic attention FLOP per step / step
+time; roofline = the prefill kernel alone (HIP events on the launch stream).
+cpu_baseline = the fp64 oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "rel-attn prefill TFLOP/s & decode KV GB/s per MI355X (% of roofline)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+HEAD_DIM = 128
+
+
+def valid_pairs(q_len, seq_len, window):
+    """Number of (query, key) pairs inside the causal window for one head."""
+    pos = np.arange(seq_len - q_len, seq_len, dtype=np.int64)
+    n = pos + 1
+    if window > 0:
+        n = np.minimum(n, window)
+    return int(n.sum())
+
+
+class DeviceCase:
+    """Device tensors of one synth case in the library's layouts."""
+
+    def __init__(self, case, torch):
+        import attention_sconv_amd as ink
+        from attention_sconv_amd import kvcache
+        self.case = c = case
+        td = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(td)
+        idev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        self.dt = ink.BF16 if c.dtype == "bf16" else ink.FP32
+        self.q, self.k_pre, self.v_pre = dev(c.q), dev(c.k_pre), dev(c.v_pre)
+        self.conv_w, self.conv_state, self.bias = dev(c.conv_w), dev(c.conv_state), dev(c.bias)
+        self.state_slot, self.cu = idev(c.state_slot), idev(c.cu_seqlens)
+        self.slot_mapping, self.block_table = idev(c.slot_mapping), idev(c.block_table)
+        self.seq_lens = idev(c.seq_lens)
+        if c.past_k is not None:
+            pk = c.past_k if torch.is_tensor(c.past_k) else dev(c.past_k)
+            pv = c.past_v if torch.is_tensor(c.past_v) else dev(c.past_v)
+            self.k_cache, self.v_cache = kvcache.from_slots(pk, pv)
+            del pk, pv
+            c.past_k = c.past_v = None
+        else:
+            self.k_cache, self.v_cache = kvcache.alloc(c.num_blocks, c.num_kv_heads, c.dtype)
+            self.k_cache.zero_()
+            self.v_cache.zero_()
+        self.out = torch.empty_like(self.q)
+        self.desc = ink.make_desc(self.dt, c.num_q_heads, c.num_kv_heads, c.window, c.bias_len)
+        self.ink = ink
+
+    def sconv(self):
+        c = self.case
+        self.ink.inkattn_sconv(self.dt, c.num_kv_heads, HEAD_DIM, len(c.q_lens), c.num_tokens,
+                               int(c.q_lens.max()), self.k_pre, self.v_pre, self.conv_w,
+                               self.conv_state, self.state_slot, self.cu, self.slot_mapping,
+                               self.k_cache, self.v_cache)
+
+    def prefill(self):
+        c = self.case
+        self.ink.inkattn_relattn_prefill(self.desc, len(c.q_lens), c.num_tokens,
+                                         int(c.q_lens.max()), self.q, self.k_cache,
+                                         self.v_cache, self.block_table,
+                                         self.block_table.shape[1], self.cu, self.seq_lens,
+                                         self.bias, self.out, None)
+
+    def setup_decode(self, torch):
+        c = self.case
+        B, L = len(c.q_lens), int(c.seq_lens.max())
+        self.num_splits = self.ink.inkattn_relattn_decode_num_splits(self.desc, B, L)
+        self.ws_bytes = self.ink.inkattn_relattn_decode_workspace_size(self.desc, B, L, 0)
+        self.ws = torch.empty(self.ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
+
+    def decode(self):
+        c = self.case
+        self.ink.inkattn_relattn_decode(self.desc, len(c.q_lens), int(c.seq_lens.max()),
+                                        self.q, self.k_cache, self.v_cache, self.block_table,
+                                        self.block_table.shape[1], self.seq_lens, self.bias,
+                                        self.out, None, 0, self.ws, self.ws_bytes)
+
+
+def time_region(torch, fn_step, fn_kernel, steps, warmup):
+    """Run warmup untimed steps, then `steps` timed steps.  Returns
+    (ms per step, mean ms of the kernel of interest), the latter from event
+    pairs recorded around that kernel on the launch stream."""
+    for _ in range(warmup):
+        fn_step(None)
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        fn_step(pairs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    ms_kernel = sum(a.elapsed_time(b) for a, b in pairs) / steps
+    return ms_step, ms_kernel
+
+
+def cpu_baseline(case, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the prefill workload: the whole
+    sconv of the chunk, then attention rows (all heads) in blocks of 256
+    spread over the sequence until the time budget is used."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    c = case
+    G = c.num_q_heads // c.num_kv_heads
+    T = int(c.q_lens[0])
+    t_start = time.perf_counter()
+    k_new, v_new, _ = oracle.sconv_batch(c.k_pre, c.v_pre, c.conv_w, c.conv_state,
+                                         c.state_slot, c.cu_seqlens)
+    K = k_new.reshape(T, c.num_kv_heads, HEAD_DIM)
+    V = v_new.reshape(T, c.num_kv_heads, HEAD_DIM)
+    flops = 0
+    rows_done = 0
+    starts = np.linspace(0, T - 256, 16).astype(int)
+    for s in starts:
+        rows = np.arange(s, s + 256)
+        oracle.relattn_prefill(c.q, K, V, c.bias, c.window, G, rows=rows)
+        n = rows + 1 if c.window == 0 else np.minimum(rows + 1, c.window)
+        flops += int(n.sum()) * 4 * HEAD_DIM * c.num_q_heads
+        rows_done += len(rows)
+        if time.perf_counter() - t_start > budget_s:
+            break
+    dt = time.perf_counter() - t_start
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"sconv of all {T} tokens + attention of {rows_done} of {T} query rows "
+                      f"(all {c.num_q_heads} heads) in {dt:.1f} s, fp64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU split is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+
+    # ---------------- prefill: sconv + prefill on the 8K SWA workload
+    wl = synth.WORKLOADS["swa_prefill_8k"]
+    case = synth.workload_case(wl, seed=0)
+    dc = DeviceCase(case, torch)
+    pairs = valid_pairs(wl.q_len, wl.seq_len, wl.window) * wl.num_q_heads * wl.batch
+    flop = 4 * HEAD_DIM * pairs
+
+    def step(ev):
+        dc.sconv()
+        if ev is not None:
+            ev[0].record()
+        dc.prefill()
+        if ev is not None:
+            ev[1].record()
+
+    print(f"[bench] prefill {wl.name}: warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+    ms_step, ms_prefill = time_region(torch, step, None, args.steps, args.warmup)
+    value = flop / (ms_step * 1e-3) / 1e12
+    achieved = flop / (ms_prefill * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name + ": " + wl.description + ", paged KV block 128, "
+                   "step = sconv + prefill", "global_batch": wl.batch,
+                   "seq_len": wl.seq_len, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel<bf16>", "ms": round(ms_prefill, 4),
+                     "algorithmic_flop": flop},
+    }
+
+    # ---------------- decode: sconv (1 token/seq) + split-K decode, 16K SWA
+    if not args.no_decode:
+        del dc
+        torch.cuda.empty_cache()
+        dwl = synth.WORKLOADS["swa_decode_16k"]
+        dcase = synth.workload_case(dwl, seed=0, past_device="cuda")
+        dd = DeviceCase(dcase, torch)
+        dd.setup_decode(torch)
+        kv_bytes = dwl.batch * dwl.num_kv_heads * 2 * min(dwl.window, dwl.seq_len) * HEAD_DIM * 2
+
+        def dstep(ev):
+            dd.sconv()
+            if ev is not None:
+                ev[0].record()
+            dd.decode()
+            if ev is not None:
+                ev[1].record()
+
+        print(f"[bench] decode {dwl.name}", file=sys.stderr, flush=True)
+        d_ms_step, d_ms = time_region(torch, dstep, None, max(args.steps, 20), args.warmup)
+        gbs = kv_bytes / (d_ms * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": dwl.name + ": " + dwl.description,
+            "ms_per_step": round(d_ms_step, 4), "ms_decode": round(d_ms, 4),
+            "num_splits": dd.num_splits,
+            "kv_bytes": kv_bytes, "achieved": round(gbs, 1), "unit": "GB/s",
+            "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "note": "L2/MALL not flushed between steps",
+        }
+        del dd
+
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(case)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

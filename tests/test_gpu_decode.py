@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import GpuCase, TOL, assert_close, host, oracle_kv, oracle_sconv
+from gpu_util import GpuCase, assert_close, assert_parity, host, oracle_kv, oracle_sconv
 
 pytestmark = pytest.mark.gpu
 
@@ -33,9 +33,8 @@ def _run_and_check(case, num_splits=0, seqs=None):
     torch.cuda.synchronize()
     want_o, want_l = _expected(case, seqs)
     sel = list(range(len(case.q_lens))) if seqs is None else list(seqs)
-    tol = TOL[case.dtype]
-    e1 = assert_close(host(out)[sel], want_o, tol, "out")
-    e2 = assert_close(host(lse)[sel], want_l, tol, "lse")
+    e1 = assert_parity(host(out)[sel], want_o, case.dtype, "out")
+    e2 = assert_parity(host(lse)[sel], want_l, case.dtype, "lse")
     return gc, out, lse, (e1, e2)
 
 

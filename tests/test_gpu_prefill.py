@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import GpuCase, TOL, assert_close, host, oracle_kv, oracle_sconv
+from gpu_util import GpuCase, assert_close, assert_parity, host, oracle_kv, oracle_sconv
 
 pytestmark = pytest.mark.gpu
 
@@ -37,9 +37,8 @@ def _run_and_check(case, rows_per_seq=None):
     out, lse = gc.prefill()
     torch.cuda.synchronize()
     toks, want_o, want_l = _expected(case, rows_per_seq)
-    tol = TOL[case.dtype]
-    assert_close(host(out)[toks], want_o, tol, "out")
-    assert_close(host(lse)[toks], want_l, tol, "lse")
+    assert_parity(host(out)[toks], want_o, case.dtype, "out")
+    assert_parity(host(lse)[toks], want_l, case.dtype, "lse")
     return gc, out, lse
 
 
