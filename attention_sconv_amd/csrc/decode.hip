@@ -38,15 +38,6 @@ constexpr int kDecodeWaves = 4;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 
 template <typename T>
-__device__ __forceinline__ Frag8<T> zero_tail(const Frag8<T>& f, int nvalid) {
-  // keep elements e < nvalid, zero the rest
-  float x[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = e < nvalid ? f.get(e) : 0.0f;
-  return Frag8<T>::pack(x);
-}
-
-template <typename T>
 __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     int Hq, int Hkv, int window, int R, int S, const T* __restrict__ q,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
@@ -170,7 +161,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     if (blk == blk_last && (L & (kPage - 1)) != 0) {
       const int nvalid = L - (blk * kPage + key_lane);
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) vf[dt] = zero_tail(vf[dt], nvalid);
+      for (int dt = 0; dt < 8; ++dt) vf[dt] = vf[dt].keep_first(nvalid);
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] = mfma16(vf[dt], pf, o[dt]);

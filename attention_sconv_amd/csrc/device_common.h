@@ -40,12 +40,16 @@ __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) {
   return __uint_as_float(uint32_t(x.bits) << 16);
 }
-// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
@@ -73,9 +77,18 @@ template <> struct Frag8<bf16> {
   __device__ __forceinline__ static Frag8 pack(const float* x) {
     Frag8 f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      f.v[i] = uint32_t(f32_to_bf16_bits(x[2 * i])) |
-               (uint32_t(f32_to_bf16_bits(x[2 * i + 1])) << 16);
+    for (int i = 0; i < 4; ++i) f.v[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    return f;
+  }
+  // Keep elements e < n, zero the others (a per-lane select, no branch).
+  __device__ __forceinline__ Frag8 keep_first(int n) const {
+    Frag8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (2 * i < n) ? 0x0000ffffu : 0u;
+      const uint32_t hi = (2 * i + 1 < n) ? 0xffff0000u : 0u;
+      f.v[i] = v[i] & (lo | hi);
+    }
     return f;
   }
   __device__ __forceinline__ bf16x8_t as_mfma() const {
@@ -105,7 +118,25 @@ template <> struct Frag8<float> {
     f.hi = f32x4{x[4], x[5], x[6], x[7]};
     return f;
   }
+  __device__ __forceinline__ Frag8 keep_first(int n) const {
+    Frag8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f.lo[e] = e < n ? lo[e] : 0.0f;
+      f.hi[e] = e + 4 < n ? hi[e] : 0.0f;
+    }
+    return f;
+  }
 };
+
+// Store 4 consecutive outputs (8 B for bf16, 16 B for fp32).
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
 
 // 32x32 output, contracts 16 k-values (lane group lane/32 holds k = 8G..8G+7).
 __device__ __forceinline__ f32x16 mfma32(const Frag8<bf16>& a, const Frag8<bf16>& b, f32x16 c) {

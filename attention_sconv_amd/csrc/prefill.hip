@@ -145,24 +145,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
     const int phys = btab[J0 / kPage];
     const int koff = J0 % kPage;
     const size_t tile = ((size_t)phys * A.Hkv + kvg) * (size_t)(kPage * kHeadDim);
+    // The whole 64-key slice lies inside one allocated page, so every load is
+    // in bounds; keys >= seq_len (only in the sequence's last tile) hold no
+    // data and are zeroed so that garbage cannot reach the products.
+    const bool tail = J0 + kBK > seq_len;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int F = tid + kThreads * p;
       const int r = F >> 4, f = F & 15;                   // K: 64 rows x 16 fragments
-      s.k[p] = (J0 + r < seq_len) ? Frag8<T>::load(kc + tile + (size_t)(koff + r) * kHeadDim + 8 * f)
-                                  : Frag8<T>::zero();
+      s.k[p] = Frag8<T>::load(kc + tile + (size_t)(koff + r) * kHeadDim + 8 * f);
       const int d = F >> 3, fv = F & 7;                   // V^T: 128 rows x 8 fragments
-      const int nvalid = seq_len - (J0 + 8 * fv);
-      if (nvalid >= 8) {
-        s.v[p] = Frag8<T>::load(vc + tile + (size_t)d * kPage + koff + 8 * fv);
-      } else if (nvalid <= 0) {
-        s.v[p] = Frag8<T>::zero();
-      } else {
-        const Frag8<T> raw = Frag8<T>::load(vc + tile + (size_t)d * kPage + koff + 8 * fv);
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = e < nvalid ? raw.get(e) : 0.0f;
-        s.v[p] = Frag8<T>::pack(x);
+      s.v[p] = Frag8<T>::load(vc + tile + (size_t)d * kPage + koff + 8 * fv);
+      if (tail) {
+        s.k[p] = s.k[p].keep_first(J0 + r < seq_len ? 8 : 0);
+        s.v[p] = s.v[p].keep_first(seq_len - (J0 + 8 * fv));
       }
     }
     if (tid < kBand) {
@@ -290,11 +286,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = 32 * dt + 8 * q4 + 4 * lg;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) op[d + r] = from_f32<T>(o[dt][4 * q4 + r] * inv);
-    }
+    for (int q4 = 0; q4 < 4; ++q4)
+      store4(op + 32 * dt + 8 * q4 + 4 * lg, o[dt][4 * q4] * inv, o[dt][4 * q4 + 1] * inv,
+             o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
   if (A.lse != nullptr && lg == 0)
     A.lse[(size_t)(tok0 + row0 + a_row) * A.Hq + h] = (m_used + fast_log2(lt)) * kLn2;
 }
