@@ -8,7 +8,7 @@
 // "sheared" bias that follows the diagonal structure).  The logit used here
 // is  q_i.k_j / sqrt(128) + bias[h][min(i-j, R-1)].
 //
-// Design (gfx950, one work-group = 4 waves = 128 query rows of one q-head):
+// Design (gfx950, one work-group = 8 waves = 256 query rows of one q-head):
 // * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 (fp32 storage:
 //   v_mfma_f32_32x32x2_f32 on the same fragments).  Wave w owns query rows
 //   32w .. 32w+31 as the 32 MFMA columns, so every softmax row statistic is
@@ -17,8 +17,8 @@
 //   16-byte XOR swizzle (conflict-free fragment reads), double-buffered with
 //   one barrier per tile; the next tile's loads are in flight while the
 //   current tile is computed.
-// * Sheared bias: for a (128-query, 64-key) tile the relative distances form
-//   a band of 191 values.  The band, pre-multiplied by sqrt(128) and holding
+// * Sheared bias: for a (256-query, 64-key) tile the relative distances form
+//   a band of 319 values.  The band, pre-multiplied by sqrt(128) and holding
 //   -inf where the key is outside the causal window, is written to LDS once
 //   per tile (four copies shifted by one entry so every lane's eight
 //   consecutive distances are one aligned 32-byte read) and loaded straight
@@ -41,14 +41,18 @@ namespace inkattn {
 
 namespace {
 
-constexpr int kBQ = 128;                 // query rows per work-group
-constexpr int kBK = 64;                  // keys per KV tile
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBand = kBQ + kBK - 1;     // 191 distinct distances per tile
-constexpr int kBandPad = 192;
+constexpr int kBQ = 32 * kWaves;         // query rows per work-group (32 per wave)
+constexpr int kBK = 64;                  // keys per KV tile
+constexpr int kBand = kBQ + kBK - 1;     // 319 distinct distances per tile
+constexpr int kBandPad = kBand + 1;
+constexpr int kStageFrags = kBK * kHeadDim / 8 / kThreads;   // fragments per thread per tile
 constexpr int kXcds = 8;
 constexpr float kRescaleSlack = 8.0f;    // log2 units
+static_assert(kStageFrags * kThreads * 8 == kBK * kHeadDim, "staging covers one tile");
+static_assert((kBQ - 1) % 4 == 3, "band copy selection assumes kBQ % 4 == 0");
+static_assert(kBand <= kThreads, "one band entry per thread");
 
 template <typename T>
 struct PrefillSmem {
@@ -81,7 +85,7 @@ __device__ __forceinline__ int keyperm(int r) {
 
 template <typename T>
 struct Stage {
-  Frag8<T> k[4], v[4];
+  Frag8<T> k[kStageFrags], v[kStageFrags];
   float band;
 };
 
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
     // data and are zeroed so that garbage cannot reach the products.
     const bool tail = J0 + kBK > seq_len;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < kStageFrags; ++p) {
       const int F = tid + kThreads * p;
       const int r = F >> 4, f = F & 15;                   // K: 64 rows x 16 fragments
       s.k[p] = Frag8<T>::load(kc + tile + (size_t)(koff + r) * kHeadDim + 8 * f);
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   };
   auto stage_store = [&](int buf, const Stage<T>& s) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < kStageFrags; ++p) {
       const int F = tid + kThreads * p;
       const int r = F >> 4, f = F & 15;
       s.k[p].store(&sm.k[buf][r * kHeadDim + 8 * (f ^ (r & 15))]);
