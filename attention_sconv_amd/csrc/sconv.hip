@@ -10,10 +10,11 @@
 //
 // Work split: grid (token chunk, sequence, K|V); each thread owns 8
 // consecutive channels (one 16-byte bf16 vector, two for fp32), so a wave
-// reads a 1 KiB channel-contiguous row per token (Hkv = 4), and walks up to
-// kChunk tokens of one sequence with the last three inputs held in
-// registers.  Only the thread that handles a sequence's first chunk touches
-// that sequence's state, so the in-place state update is race-free.
+// reads a 1 KiB channel-contiguous row per token (Hkv = 4), and 8 tokens of
+// one sequence, loading them and the 3-token halo up front so the loads are
+// in flight together; the 4-tap window then runs in registers.  Only the
+// thread that handles a sequence's first chunk touches that sequence's
+// state, so the in-place state update is race-free.
 // Memory-bound: every input byte is read once (plus a 3-row halo per chunk)
 // and every output byte written once.
 #include "device_common.h"
@@ -21,7 +22,8 @@
 
 namespace inkattn {
 
-constexpr int kSconvChunk = 16;
+constexpr int kSconvTok = 8;          // tokens per thread
+constexpr int kSconvRows = 4;         // token chunks per work-group (blockDim.y)
 
 template <typename T>
 __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
     T* __restrict__ v_cache) {
   const int which = blockIdx.z;              // 0 = keys, 1 = values
   const int b = blockIdx.y;
-  const int r0 = blockIdx.x * kSconvChunk;   // first token of the chunk (relative)
+  const int r0 = (blockIdx.x * blockDim.y + threadIdx.y) * kSconvTok;   // first token (relative)
   const int c0 = threadIdx.x * 8;
   const int t_begin = cu_seqlens[b];
   const int n = cu_seqlens[b + 1] - t_begin;
@@ -42,10 +44,24 @@ __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
   const T* wp = conv_w + ((size_t)which * C + c0) * 4;
   T* st = conv_state + ((size_t)state_slot[b] * 2 + which) * 3 * C + c0;
 
+  // All inputs of the chunk and its 3-token halo are loaded up front (the
+  // halo before the sequence start comes from the cached state).
+  Frag8<T> xs[kSconvTok + 3];
+#pragma unroll
+  for (int k = 0; k < kSconvTok + 3; ++k) {
+    const int rel = r0 - 3 + k;
+    xs[k] = rel < 0 ? Frag8<T>::load(st + (size_t)(rel + 3) * C)
+                    : (rel < n ? Frag8<T>::load(x + (size_t)rel * C) : Frag8<T>::zero());
+  }
+  int slot[kSconvTok];
+#pragma unroll
+  for (int t = 0; t < kSconvTok; ++t)
+    slot[t] = r0 + t < n ? slot_mapping[t_begin + r0 + t] : -1;
+
   float w[8][4];
   {
-    Frag8<T> f0 = Frag8<T>::load(wp), f1 = Frag8<T>::load(wp + 8),
-             f2 = Frag8<T>::load(wp + 16), f3 = Frag8<T>::load(wp + 24);
+    const Frag8<T> f0 = Frag8<T>::load(wp), f1 = Frag8<T>::load(wp + 8),
+                   f2 = Frag8<T>::load(wp + 16), f3 = Frag8<T>::load(wp + 24);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const Frag8<T>& f = e < 2 ? f0 : e < 4 ? f1 : e < 6 ? f2 : f3;
@@ -54,45 +70,56 @@ __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
     }
   }
 
-  // Inputs of the three tokens before r0: from this chunk's sequence, or
-  // from the cached state for positions before the chunk start.
-  Frag8<T> h0, h1, h2;
-  {
-    Frag8<T> hk[3];
+  float y[kSconvTok][8];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int rel = r0 - 3 + k;
-      hk[k] = rel >= 0 ? Frag8<T>::load(x + (size_t)rel * C)
-                       : Frag8<T>::load(st + (size_t)(rel + 3) * C);
-    }
-    h0 = hk[0]; h1 = hk[1]; h2 = hk[2];
-  }
+  for (int t = 0; t < kSconvTok; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      y[t][e] = w[e][0] * xs[t].get(e) + w[e][1] * xs[t + 1].get(e) +
+                w[e][2] * xs[t + 2].get(e) + w[e][3] * xs[t + 3].get(e);
 
   const int kvh = c0 / kHeadDim;
   const int dd = c0 % kHeadDim;
-  const int r_end = min(r0 + kSconvChunk, n);
-  for (int r = r0; r < r_end; ++r) {
-    const Frag8<T> cur = Frag8<T>::load(x + (size_t)r * C);
-    float y[8];
+  if (which == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      y[e] = w[e][0] * h0.get(e) + w[e][1] * h1.get(e) + w[e][2] * h2.get(e) +
-             w[e][3] * cur.get(e);
-    const int slot = slot_mapping[t_begin + r];
-    const size_t tile = (size_t)(slot >> 7) * Hkv + kvh;
-    const int off = slot & (kPage - 1);
-    if (which == 0) {
-      Frag8<T>::pack(y).store(k_cache + (tile * kPage + off) * kHeadDim + dd);
-    } else {
-      T* vt = v_cache + (tile * kHeadDim + dd) * kPage + off;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(size_t)e * kPage] = from_f32<T>(y[e]);
+    for (int t = 0; t < kSconvTok; ++t) {
+      if (slot[t] < 0) continue;
+      const size_t tile = (size_t)(slot[t] >> 7) * Hkv + kvh;
+      Frag8<T>::pack(y[t]).store(k_cache + (tile * kPage + (slot[t] & (kPage - 1))) * kHeadDim + dd);
     }
-    h0 = h1; h1 = h2; h2 = cur;
+  } else {
+    // V is stored transposed per page.  When the 8 tokens occupy 8
+    // consecutive slots starting at a multiple of 8 (always the case for a
+    // fresh prefill), each channel's 8 values are one 16-byte store;
+    // otherwise they are scattered element by element.
+    bool run = slot[0] >= 0 && (slot[0] & 7) == 0;
+#pragma unroll
+    for (int t = 1; t < kSconvTok; ++t) run = run && slot[t] == slot[0] + t;
+    if (run) {
+      const size_t tile = (size_t)(slot[0] >> 7) * Hkv + kvh;
+      T* vt = v_cache + (tile * kHeadDim + dd) * kPage + (slot[0] & (kPage - 1));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float col[kSconvTok];
+#pragma unroll
+        for (int t = 0; t < kSconvTok; ++t) col[t] = y[t][e];
+        Frag8<T>::pack(col).store(vt + (size_t)e * kPage);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < kSconvTok; ++t) {
+        if (slot[t] < 0) continue;
+        const size_t tile = (size_t)(slot[t] >> 7) * Hkv + kvh;
+        T* vt = v_cache + (tile * kHeadDim + dd) * kPage + (slot[t] & (kPage - 1));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vt[(size_t)e * kPage] = from_f32<T>(y[t][e]);
+      }
+    }
   }
 
   if (r0 == 0) {
-    // New state = last three rows of [old state; chunk inputs].
+    // New state = last three rows of [old state; sequence inputs].  Only the
+    // thread that owns the first chunk touches the state.
     Frag8<T> ns[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
@@ -111,8 +138,13 @@ hipError_t launch_sconv(int dtype, int Hkv, int num_seqs, int max_chunk_len,
                         const int32_t* cu_seqlens, const int32_t* slot_mapping,
                         void* k_cache, void* v_cache, hipStream_t stream) {
   const int C = Hkv * kHeadDim;
-  dim3 grid((max_chunk_len + kSconvChunk - 1) / kSconvChunk, num_seqs, 2);
-  dim3 block(C / 8);
+  const int per_block = kSconvTok * kSconvRows;
+  dim3 grid((max_chunk_len + per_block - 1) / per_block, num_seqs, 2);
+  dim3 block(C / 8, kSconvRows);
+  if (block.x * block.y > 1024) {                            // Hkv > 16
+    block.y = 1024 / block.x;
+    grid.x = (max_chunk_len + kSconvTok * block.y - 1) / (kSconvTok * block.y);
+  }
   if (dtype == kDtypeBf16) {
     hipLaunchKernelGGL(sconv_cache_write_kernel<bf16>, grid, block, 0, stream, C, Hkv,
                        (const bf16*)k_in, (const bf16*)v_in, (const bf16*)conv_w,
