@@ -46,7 +46,11 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBQ = 32 * kWaves;         // query rows per work-group (32 per wave)
 constexpr int kBK = 64;                  // keys per KV tile
 constexpr int kBand = kBQ + kBK - 1;     // 319 distinct distances per tile
-constexpr int kBandPad = kBand + 1;
+// Copy stride of the band in LDS: 336 words = 16 (mod 64), so the four
+// copies start 4 bank groups apart and the 16 lanes of a quarter-wave
+// (4 copies x 4 consecutive 16-byte groups) hit 16 distinct bank groups.
+constexpr int kBandPad = 336;
+static_assert(kBandPad >= kBand + 1 && kBandPad % 64 == 16, "band copy stride");
 constexpr int kStageFrags = kBK * kHeadDim / 8 / kThreads;   // fragments per thread per tile
 constexpr int kXcds = 8;
 constexpr float kRescaleSlack = 8.0f;    // log2 units

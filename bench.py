@@ -124,10 +124,10 @@ def time_region(torch, fn_step, fn_kernel, steps, warmup):
     return ms_step, ms_kernel
 
 
-def cpu_baseline(case, budget_s=12.0):
-    """The fp64 oracle on a bounded sample of the prefill workload: the whole
-    sconv of the chunk, then attention rows (all heads) in blocks of 256
-    spread over the sequence until the time budget is used."""
+def cpu_baseline(case, budget_s=10.0):
+    """The fp64 oracle on the prefill workload, timed on the host cores: the
+    sconv of the chunk, then attention of all query rows (all heads) in
+    blocks of 256, repeated until at least ``budget_s`` seconds of work."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -137,27 +137,28 @@ def cpu_baseline(case, budget_s=12.0):
     c = case
     G = c.num_q_heads // c.num_kv_heads
     T = int(c.q_lens[0])
-    t_start = time.perf_counter()
-    k_new, v_new, _ = oracle.sconv_batch(c.k_pre, c.v_pre, c.conv_w, c.conv_state,
-                                         c.state_slot, c.cu_seqlens)
-    K = k_new.reshape(T, c.num_kv_heads, HEAD_DIM)
-    V = v_new.reshape(T, c.num_kv_heads, HEAD_DIM)
     flops = 0
     rows_done = 0
-    starts = np.linspace(0, T - 256, 16).astype(int)
-    for s in starts:
-        rows = np.arange(s, s + 256)
-        oracle.relattn_prefill(c.q, K, V, c.bias, c.window, G, rows=rows)
-        n = rows + 1 if c.window == 0 else np.minimum(rows + 1, c.window)
-        flops += int(n.sum()) * 4 * HEAD_DIM * c.num_q_heads
-        rows_done += len(rows)
-        if time.perf_counter() - t_start > budget_s:
-            break
+    passes = 0
+    t_start = time.perf_counter()
+    while time.perf_counter() - t_start < budget_s and passes < 8:
+        k_new, v_new, _ = oracle.sconv_batch(c.k_pre, c.v_pre, c.conv_w, c.conv_state,
+                                             c.state_slot, c.cu_seqlens)
+        K = k_new.reshape(T, c.num_kv_heads, HEAD_DIM)
+        V = v_new.reshape(T, c.num_kv_heads, HEAD_DIM)
+        for s in range(0, T, 256):
+            rows = np.arange(s, min(s + 256, T))
+            oracle.relattn_prefill(c.q, K, V, c.bias, c.window, G, rows=rows)
+            n = rows + 1 if c.window == 0 else np.minimum(rows + 1, c.window)
+            flops += int(n.sum()) * 4 * HEAD_DIM * c.num_q_heads
+            rows_done += len(rows)
+        passes += 1
     dt = time.perf_counter() - t_start
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"sconv of all {T} tokens + attention of {rows_done} of {T} query rows "
-                      f"(all {c.num_q_heads} heads) in {dt:.1f} s, fp64 numpy"}
+            "sample": f"{passes} full pass(es) of the workload (sconv of {T} tokens + "
+                      f"attention of all {T} rows x {c.num_q_heads} heads) in {dt:.1f} s, "
+                      f"fp64 numpy"}
 
 
 def main():
@@ -167,6 +168,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the bench, run one plain device-to-device copy of this "
+                         "many bytes (reference kernel for HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -254,6 +258,15 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(case)
+
+    if args.copy_bytes > 0:
+        n = args.copy_bytes // 4
+        src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_bytes"] = n * 4
 
     print(json.dumps(result), flush=True)
 
