@@ -91,6 +91,21 @@ template <> struct Frag8<bf16> {
     }
     return f;
   }
+  // acc + sum of the 8 (rounded) elements, two per v_dot2_f32_bf16 against
+  // (1.0, 1.0).  Written as inline VOP3P: with the builtin, the compiler in
+  // ROCm 7.2 emits the VOP2 form v_dot2c_f32_bf16 and, when the source is a
+  // word of a 128-bit register tuple, reads the tuple's first register for
+  // every word.
+  __device__ __forceinline__ float sum_into(float acc) const {
+    const uint32_t ones = 0x3f803f80u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float r;
+      asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(r) : "v"(v[i]), "v"(ones), "v"(acc));
+      acc = r;
+    }
+    return acc;
+  }
   __device__ __forceinline__ bf16x8_t as_mfma() const {
     return __builtin_bit_cast(bf16x8_t, v);
   }
@@ -117,6 +132,9 @@ template <> struct Frag8<float> {
     f.lo = f32x4{x[0], x[1], x[2], x[3]};
     f.hi = f32x4{x[4], x[5], x[6], x[7]};
     return f;
+  }
+  __device__ __forceinline__ float sum_into(float acc) const {
+    return acc + ((lo[0] + lo[1]) + (lo[2] + lo[3])) + ((hi[0] + hi[1]) + (hi[2] + hi[3]));
   }
   __device__ __forceinline__ Frag8 keep_first(int n) const {
     Frag8 f;
@@ -162,6 +180,19 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 __device__ __forceinline__ float wave_shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
+}
+
+// Reductions over the lane pair (l, l ^ 32) with v_permlane32_swap: after
+// the swap one result register holds lane l's value and the other its
+// partner's (which is which depends on the half), so max/sum of the two is
+// the pair reduction in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 }  // namespace inkattn

@@ -93,6 +93,14 @@ struct Stage {
   float band;
 };
 
+// LDS swizzles (16-byte fragment slot = fragment ^ swizzle(row)).  ds_read_b128
+// is served a quarter-wave (16 lanes) at a time over 64 banks, so the 16
+// lanes of a quarter must hit 16 distinct 16-byte bank groups.
+// K rows are 256 B: a quarter reads rows keyperm(0..15) = all residues mod 16.
+__device__ __forceinline__ int kswz(int r) { return r & 15; }
+// V^T rows are 128 B (two rows per bank cycle): a quarter reads rows d..d+15.
+__device__ __forceinline__ int vswz(int d) { return ((d >> 1) & 7); }
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   __shared__ PrefillSmem<T> sm;
@@ -180,9 +188,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
     for (int p = 0; p < kStageFrags; ++p) {
       const int F = tid + kThreads * p;
       const int r = F >> 4, f = F & 15;
-      s.k[p].store(&sm.k[buf][r * kHeadDim + 8 * (f ^ (r & 15))]);
+      s.k[p].store(&sm.k[buf][r * kHeadDim + 8 * (f ^ kswz(r))]);
       const int d = F >> 3, fv = F & 7;
-      s.v[p].store(&sm.vt[buf][d * kBK + 8 * (fv ^ ((d >> 1) & 7))]);
+      s.v[p].store(&sm.vt[buf][d * kBK + 8 * (fv ^ vswz(d))]);
     }
     if (tid < kBand) {
 #pragma unroll
@@ -213,6 +221,23 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
     const bool has_next = jt < jt_hi;
     if (has_next) stage_load(jt + 1, st);
 
+    // LDS fragment reads run ahead of the MFMAs that consume them (K two
+    // steps ahead, the first V slab before the softmax, later V slabs one
+    // slab ahead) so that LDS latency overlaps matrix work.
+    auto kfrag = [&](int ks, int t) {
+      const int kr = 32 * t + kp;
+      return Frag8<T>::load(&sm.k[buf][kr * kHeadDim + 8 * ((2 * ks + lg) ^ kswz(kr))]);
+    };
+    auto vfrag = [&](int slab, int dt) {
+      const int dr = 32 * dt + lq;
+      return Frag8<T>::load(&sm.vt[buf][dr * kBK + 8 * ((2 * slab + lg) ^ vswz(dr))]);
+    };
+    Frag8<T> kq[3][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) kq[j][t] = kfrag(j, t);
+
     // S^T accumulators start as the sheared bias band.
     f32x16 acc[2];
 #pragma unroll
@@ -230,14 +255,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
         }
       }
 
+    // (sched_barrier keeps the compiler from sinking the reads back next to
+    // their uses, which would expose the full LDS latency on every MFMA.)
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks + 2 < 8) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int kr = 32 * t + kp;
-        const Frag8<T> kf = Frag8<T>::load(&sm.k[buf][kr * kHeadDim + 8 * ((2 * ks + lg) ^ (kr & 15))]);
-        acc[t] = mfma32(kf, qf[ks], acc[t]);
+        for (int t = 0; t < 2; ++t) kq[(ks + 2) % 3][t] = kfrag(ks + 2, t);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) acc[t] = mfma32(kq[ks % 3][t], qf[ks], acc[t]);
+    }
+    Frag8<T> vq[2][4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) vq[0][dt] = vfrag(0, dt);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- online softmax (base 2), lazy rescale
     float mx = -INFINITY;
@@ -245,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[t][r]);
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    mx = pair_max(mx);
     const float m_tile = mx * c;
     const bool need = m_tile > m_used + kRescaleSlack;
     if (__any(need)) {
@@ -265,29 +298,29 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
       for (int hh = 0; hh < 2; ++hh) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(acc[t][8 * hh + e] * c - msub);
-          l_sum += p[e];
-        }
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(acc[t][8 * hh + e] * c - msub);
         pf[2 * t + hh] = Frag8<T>::pack(p);
+        l_sum = pf[2 * t + hh].sum_into(l_sum);     // sums the values fed to P V
       }
 
     // ---- O^T += V^T P^T
 #pragma unroll
-    for (int slab = 0; slab < 4; ++slab)
+    for (int slab = 0; slab < 4; ++slab) {
+      if (slab + 1 < 4) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int dr = 32 * dt + lq;
-        const Frag8<T> vf = Frag8<T>::load(&sm.vt[buf][dr * kBK + 8 * ((2 * slab + lg) ^ ((dr >> 1) & 7))]);
-        o[dt] = mfma32(vf, pf[slab], o[dt]);
+        for (int dt = 0; dt < 4; ++dt) vq[(slab + 1) & 1][dt] = vfrag(slab + 1, dt);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vq[slab & 1][dt], pf[slab], o[dt]);
+    }
 
     if (has_next) stage_store(buf ^ 1, st);
     __syncthreads();
   }
 
   // ---- epilogue: O^T register r of tile dt is dim 32dt + 8(r/4) + 4lg + r%4
-  const float lt = l_sum + wave_shfl_xor(l_sum, 32);
+  const float lt = pair_sum(l_sum);
   if (!row_ok) return;
   const float inv = 1.0f / lt;
   T* op = static_cast<T*>(A.out) + ((size_t)(tok0 + row0 + a_row) * A.Hq + h) * kHeadDim;
