@@ -102,6 +102,25 @@ class DeviceCase:
                                         self.out, None, 0, self.ws, self.ws_bytes)
 
 
+def recorded_traffic(profile, sources):
+    """HBM bytes per launch recorded by the rocprofv3 FETCH_SIZE/WRITE_SIZE
+    passes summarised in profiles/<profile>, or None when the kernel's
+    sources have changed since those counters were taken (hash mismatch)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    try:
+        fields = dict(l.split(":", 1) for l in open(path).read().splitlines() if ":" in l)
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    recorded = fields.get("source_sha256_16", "").split()
+    if not recorded or recorded[0] != h.hexdigest()[:16]:
+        return None
+    return int(fields["traffic_bytes_per_launch"].strip())
+
+
 def time_region(torch, fn_step, fn_kernel, steps, warmup):
     """Run warmup untimed steps, then `steps` timed steps.  Returns
     (ms per step, mean ms of the kernel of interest), the latter from event
@@ -219,7 +238,11 @@ def main():
                    "seq_len": wl.seq_len, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(
+                         "prefill_bf16_swa_prefill_8k.traffic.txt",
+                         ["attention_sconv_amd/csrc/prefill.hip",
+                          "attention_sconv_amd/csrc/device_common.h"]),
                      "kernel": "prefill_kernel<bf16>", "ms": round(ms_prefill, 4),
                      "algorithmic_flop": flop},
     }
@@ -251,6 +274,10 @@ def main():
             "num_splits": dd.num_splits,
             "kv_bytes": kv_bytes, "achieved": round(gbs, 1), "unit": "GB/s",
             "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": recorded_traffic(
+                "decode_split_bf16_swa_decode_16k.traffic.txt",
+                ["attention_sconv_amd/csrc/decode.hip",
+                 "attention_sconv_amd/csrc/device_common.h"]),
             "note": "L2/MALL not flushed between steps",
         }
         del dd
