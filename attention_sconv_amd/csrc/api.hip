@@ -12,7 +12,7 @@ using inkattn::AttnShape;
 namespace {
 
 constexpr int kCUs = 256;                  // MI355X compute units
-constexpr int kDecodeTargetGroups = 4 * kCUs;
+constexpr int kDecodeTargetGroups = 2 * kCUs;     // (seq, kv-head, split) work-groups
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -42,7 +42,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     int Hq, int Hkv, int window, int R, int S, const T* __restrict__ q,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seq_lens,
-    const T* __restrict__ bias, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    const T* __restrict__ bias, float* __restrict__ part_o, float* __restrict__ part_lse,
+    T* __restrict__ out, float* __restrict__ lse) {
   __shared__ float sm_m[kDecodeWaves][16];
   __shared__ float sm_l[kDecodeWaves][16];
   __shared__ float sm_o[kDecodeWaves][16][kHeadDim + 4];
@@ -90,7 +91,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const int phys = block_table[(size_t)b * max_blocks + blk];
     return ((size_t)phys * Hkv + kvh) * (size_t)(kPage * kHeadDim);
   };
-  auto load_page = [&](int blk, Frag8<T>* kf, Frag8<T>* vf) {
+  // Everything a page needs is loaded in one batch, one page ahead: K and V^T
+  // fragments and the 8 bias entries of this lane's keys.  Bias indices are
+  // clamped into the table (masked keys are dropped later by a select), so
+  // no load sits behind a branch and no wait drains the prefetch.
+  auto load_page = [&](int blk, Frag8<T>* kf, Frag8<T>* vf, T* bb) {
+    const int j0 = blk * kPage + key_lane;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bb[e] = bias_h[min(max(L - 1 - (j0 + e), 0), R - 1)];
     const size_t base = page_base(blk);
     const T* kt = k_cache + base;
     const T* vt = v_cache + base;
@@ -104,21 +112,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       vf[dt] = Frag8<T>::load(vt + (size_t)(16 * dt + col) * kPage + key_lane);
   };
 
-  Frag8<T> kf[8], vf[8];
-  if (my_lo < my_hi) load_page(my_lo, kf, vf);
-  for (int blk = my_lo; blk < my_hi; ++blk) {
-    Frag8<T> kn[8], vn[8];
-    if (blk + 1 < my_hi) load_page(blk + 1, kn, vn);
-
-    // Relative bias of this lane's 8 keys (distance L-1-j, clipped to R-1).
+  // One page of this wave's 32 keys: scores, online softmax, O^T += V^T P^T.
+  auto process_page = [&](int blk, const Frag8<T>* kf, Frag8<T>* vf, const T* bb) {
     const int j0 = blk * kPage + key_lane;
-    float bv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int dist = L - 1 - (j0 + e);
-      bv[e] = (head_ok && dist >= 0) ? to_f32(bias_h[min(dist, R - 1)]) * kLog2e : 0.0f;
-    }
-
     f32x4 sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -133,11 +129,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     for (int e = 0; e < 8; ++e) {
       const int j = j0 + e;
       const bool ok = head_ok && j >= kstart && j < L;
-      x[e] = ok ? sacc[e >> 2][e & 3] * c + bv[e] : -INFINITY;
+      x[e] = ok ? sacc[e >> 2][e & 3] * c + to_f32(bb[e]) * kLog2e : -INFINITY;
       mx = fmaxf(mx, x[e]);
     }
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    mx = pair_max(mx);
     const float m_new = fmaxf(m, mx);
     const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
     const float alpha = fast_exp2(m - m_sub);       // m = -inf -> 0
@@ -165,16 +161,28 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] = mfma16(vf[dt], pf, o[dt]);
+  };
 
-    if (blk + 1 < my_hi) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { kf[i] = kn[i]; vf[i] = vn[i]; }
-    }
+  // Pages alternate between two register sets, so the next page's loads are
+  // in flight while the current one is computed and no register copy (which
+  // would wait for those loads) is needed between iterations.
+  // Loads are unconditional (a page index past the split re-reads the
+  // split's last page, an L2 hit) so the memory-wait bookkeeping stays exact
+  // and each page only waits for its own loads.
+  Frag8<T> ka[8], va[8], kb[8], vb[8];
+  T ba[8], bbb[8];
+  const int last = my_hi - 1;
+  if (my_lo < my_hi) load_page(my_lo, ka, va, ba);
+  for (int blk = my_lo; blk < my_hi; blk += 2) {
+    load_page(min(blk + 1, last), kb, vb, bbb);
+    process_page(blk, ka, va, ba);
+    load_page(min(blk + 2, last), ka, va, ba);
+    if (blk + 1 < my_hi) process_page(blk + 1, kb, vb, bbb);
   }
 
   // Merge the four waves.  O^T register r of tile dt is dim 16dt + 4G + r.
   float lt = l + wave_shfl_xor(l, 16);
-  lt += wave_shfl_xor(lt, 32);
+  lt = pair_sum(lt);
   if (grp == 0) {
     sm_m[wave][col] = m;
     sm_l[wave][col] = lt;
@@ -204,8 +212,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       num += sc * sm_o[w][hh][d];
       den += sc * sm_l[w][hh];
     }
-    part_o[row * kHeadDim + d] = num / den;
-    if (d == 0) part_lse[row] = (M + fast_log2(den)) * kLn2;
+    if (S == 1) {
+      // A single split is the whole key range: write the result directly
+      // (no merge pass).
+      const size_t orow = (size_t)b * Hq + kvh * G + hh;
+      out[orow * kHeadDim + d] = from_f32<T>(num / den);
+      if (lse != nullptr && d == 0) lse[orow] = (M + fast_log2(den)) * kLn2;
+    } else {
+      part_o[row * kHeadDim + d] = num / den;
+      if (d == 0) part_lse[row] = (M + fast_log2(den)) * kLn2;
+    }
   }
 }
 
@@ -244,16 +260,20 @@ hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_splits, const
     hipLaunchKernelGGL(decode_split_kernel<bf16>, grid, dim3(kDecodeThreads), 0, stream, s.Hq,
                        s.Hkv, s.window, s.bias_len, num_splits, (const bf16*)q,
                        (const bf16*)k_cache, (const bf16*)v_cache, block_table,
-                       max_blocks_per_seq, seq_lens, (const bf16*)bias, part_o, part_lse);
-    hipLaunchKernelGGL(decode_merge_kernel<bf16>, mgrid, dim3(kHeadDim), 0, stream, s.Hq,
-                       num_splits, part_o, part_lse, (bf16*)out, lse);
+                       max_blocks_per_seq, seq_lens, (const bf16*)bias, part_o, part_lse,
+                       (bf16*)out, lse);
+    if (num_splits > 1)
+      hipLaunchKernelGGL(decode_merge_kernel<bf16>, mgrid, dim3(kHeadDim), 0, stream, s.Hq,
+                         num_splits, part_o, part_lse, (bf16*)out, lse);
   } else {
     hipLaunchKernelGGL(decode_split_kernel<float>, grid, dim3(kDecodeThreads), 0, stream, s.Hq,
                        s.Hkv, s.window, s.bias_len, num_splits, (const float*)q,
                        (const float*)k_cache, (const float*)v_cache, block_table,
-                       max_blocks_per_seq, seq_lens, (const float*)bias, part_o, part_lse);
-    hipLaunchKernelGGL(decode_merge_kernel<float>, mgrid, dim3(kHeadDim), 0, stream, s.Hq,
-                       num_splits, part_o, part_lse, (float*)out, lse);
+                       max_blocks_per_seq, seq_lens, (const float*)bias, part_o, part_lse,
+                       (float*)out, lse);
+    if (num_splits > 1)
+      hipLaunchKernelGGL(decode_merge_kernel<float>, mgrid, dim3(kHeadDim), 0, stream, s.Hq,
+                         num_splits, part_o, part_lse, (float*)out, lse);
   }
   return hipGetLastError();
 }

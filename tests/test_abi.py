@@ -130,11 +130,11 @@ def test_decode_workspace_rules():
 
 
 def test_num_splits_heuristic():
-    # enough (seq, kv-head, split) groups for 4 per compute unit, never more
+    # enough (seq, kv-head, split) groups for 2 per compute unit, never more
     # splits than pages in the attended range
     sw = _desc(W=4096, R=4096)
-    assert ink.inkattn_relattn_decode_num_splits(sw, 64, 16384) == 4
+    assert ink.inkattn_relattn_decode_num_splits(sw, 64, 16384) == 2
     full = _desc(W=0, R=1 << 20)
-    assert ink.inkattn_relattn_decode_num_splits(full, 4, 1 << 20) == 64
+    assert ink.inkattn_relattn_decode_num_splits(full, 4, 1 << 20) == 32
     assert ink.inkattn_relattn_decode_num_splits(full, 1, 100) == 1
     assert ink.inkattn_relattn_decode_num_splits(full, 1, 300) == 3
