@@ -38,7 +38,7 @@ constexpr int kDecodeWaves = 4;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 
 template <typename T>
-__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
+__global__ __launch_bounds__(kDecodeThreads, 2) void decode_split_kernel(
     int Hq, int Hkv, int window, int R, int S, const T* __restrict__ q,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seq_lens,
