@@ -13,10 +13,10 @@
 //   v_mfma_f32_32x32x2_f32 on the same fragments).  Wave w owns query rows
 //   32w .. 32w+31 as the 32 MFMA columns, so every softmax row statistic is
 //   one lane plus its partner 32 lanes away.
-// * K and V^T tiles of 64 keys are staged global -> registers -> LDS with a
-//   16-byte XOR swizzle (conflict-free fragment reads), double-buffered with
-//   one barrier per tile; the next tile's loads are in flight while the
-//   current tile is computed.
+// * K and V^T tiles of 64 keys are staged global -> registers -> LDS in
+//   padded rows (conflict-free fragment reads at fixed offsets),
+//   double-buffered with one barrier per tile; the next tile's loads are in
+//   flight while the current tile is computed.
 // * Sheared bias: for a (256-query, 64-key) tile the relative distances form
 //   a band of 319 values.  The band, pre-multiplied by sqrt(128) and holding
 //   -inf where the key is outside the causal window, is written to LDS once
@@ -58,10 +58,20 @@ static_assert(kStageFrags * kThreads * 8 == kBK * kHeadDim, "staging covers one 
 static_assert((kBQ - 1) % 4 == 3, "band copy selection assumes kBQ % 4 == 0");
 static_assert(kBand <= kThreads, "one band entry per thread");
 
+// LDS rows are padded by one 16-byte bf16 fragment: a K row is 272 B, a V^T
+// row 144 B.  ds_read_b128 is served a quarter-wave (16 lanes) at a time over
+// 64 banks; a quarter reads one fragment column from 16 distinct rows, and
+// with these strides row r starts 17r (K) or 9r (V^T) bank groups in, which
+// is 16 distinct groups mod 16.  Unlike an XOR swizzle, padding keeps every
+// fragment read at (per-lane base + compile-time offset), so the LDS reads
+// cost no address arithmetic.
+constexpr int kKStride = kHeadDim + 8;   // elements per K row in LDS
+constexpr int kVStride = kBK + 8;        // elements per V^T row in LDS
+
 template <typename T>
 struct PrefillSmem {
-  T k[2][kBK * kHeadDim];                // [key][d], fragment f of row r at slot f ^ (r & 15)
-  T vt[2][kHeadDim * kBK];               // [d][key], fragment f of row d at slot f ^ ((d >> 1) & 7)
+  T k[2][kBK * kKStride];                // [key][d]
+  T vt[2][kHeadDim * kVStride];          // [d][key]
   float band[2][4][kBandPad];            // copy s holds band[v + s]
 };
 
@@ -92,14 +102,6 @@ struct Stage {
   Frag8<T> k[kStageFrags], v[kStageFrags];
   float band;
 };
-
-// LDS swizzles (16-byte fragment slot = fragment ^ swizzle(row)).  ds_read_b128
-// is served a quarter-wave (16 lanes) at a time over 64 banks, so the 16
-// lanes of a quarter must hit 16 distinct 16-byte bank groups.
-// K rows are 256 B: a quarter reads rows keyperm(0..15) = all residues mod 16.
-__device__ __forceinline__ int kswz(int r) { return r & 15; }
-// V^T rows are 128 B (two rows per bank cycle): a quarter reads rows d..d+15.
-__device__ __forceinline__ int vswz(int d) { return ((d >> 1) & 7); }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
@@ -162,9 +164,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
     const int koff = J0 % kPage;
     const size_t tile = ((size_t)phys * A.Hkv + kvg) * (size_t)(kPage * kHeadDim);
     // The whole 64-key slice lies inside one allocated page, so every load is
-    // in bounds; keys >= seq_len (only in the sequence's last tile) hold no
-    // data and are zeroed so that garbage cannot reach the products.
-    const bool tail = J0 + kBK > seq_len;
+    // in bounds (keys >= seq_len of the last tile are cleaned up in LDS).
 #pragma unroll
     for (int p = 0; p < kStageFrags; ++p) {
       const int F = tid + kThreads * p;
@@ -172,10 +172,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
       s.k[p] = Frag8<T>::load(kc + tile + (size_t)(koff + r) * kHeadDim + 8 * f);
       const int d = F >> 3, fv = F & 7;                   // V^T: 128 rows x 8 fragments
       s.v[p] = Frag8<T>::load(vc + tile + (size_t)d * kPage + koff + 8 * fv);
-      if (tail) {
-        s.k[p] = s.k[p].keep_first(J0 + r < seq_len ? 8 : 0);
-        s.v[p] = s.v[p].keep_first(seq_len - (J0 + 8 * fv));
-      }
     }
     if (tid < kBand) {
       const int dist = P0 - J0 + (kBQ - 1) - tid;
@@ -188,9 +184,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
     for (int p = 0; p < kStageFrags; ++p) {
       const int F = tid + kThreads * p;
       const int r = F >> 4, f = F & 15;
-      s.k[p].store(&sm.k[buf][r * kHeadDim + 8 * (f ^ kswz(r))]);
+      s.k[p].store(&sm.k[buf][r * kKStride + 8 * f]);
       const int d = F >> 3, fv = F & 7;
-      s.v[p].store(&sm.vt[buf][d * kBK + 8 * (fv ^ vswz(d))]);
+      s.v[p].store(&sm.vt[buf][d * kVStride + 8 * fv]);
     }
     if (tid < kBand) {
 #pragma unroll
@@ -216,9 +212,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   stage_store(0, st);
   __syncthreads();
 
+  // Keys >= seq_len exist only in the sequence's last tile.  They hold no
+  // data (possibly NaN), so before that tile is used its K rows and V^T
+  // columns past seq_len are zeroed in LDS: 0 * garbage must not reach O,
+  // and the masked logits must stay -inf rather than NaN.
+  const int n_tail = seq_len - jt_hi * kBK;               // valid keys of the last tile
+  auto clean_tail = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < kStageFrags; ++p) {
+      const int F = tid + kThreads * p;
+      const int r = F >> 4, f = F & 15;
+      if (r >= n_tail) Frag8<T>::zero().store(&sm.k[buf][r * kKStride + 8 * f]);
+      const int d = F >> 3, fv = F & 7;
+      if (8 * fv + 8 > n_tail) {
+        T* q8 = &sm.vt[buf][d * kVStride + 8 * fv];
+        Frag8<T>::load(q8).keep_first(n_tail - 8 * fv).store(q8);
+      }
+    }
+  };
+
   for (int jt = jt_lo; jt <= jt_hi; ++jt) {
     const int buf = (jt - jt_lo) & 1;
     const bool has_next = jt < jt_hi;
+    if (jt == jt_hi && n_tail < kBK) {          // wave-uniform, once per work-group
+      clean_tail(buf);
+      __syncthreads();
+    }
     if (has_next) stage_load(jt + 1, st);
 
     // LDS fragment reads run ahead of the MFMAs that consume them (K two
@@ -226,11 +245,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
     // slab ahead) so that LDS latency overlaps matrix work.
     auto kfrag = [&](int ks, int t) {
       const int kr = 32 * t + kp;
-      return Frag8<T>::load(&sm.k[buf][kr * kHeadDim + 8 * ((2 * ks + lg) ^ kswz(kr))]);
+      return Frag8<T>::load(&sm.k[buf][kr * kKStride + 8 * (2 * ks + lg)]);
     };
     auto vfrag = [&](int slab, int dt) {
       const int dr = 32 * dt + lq;
-      return Frag8<T>::load(&sm.vt[buf][dr * kBK + 8 * ((2 * slab + lg) ^ vswz(dr))]);
+      return Frag8<T>::load(&sm.vt[buf][dr * kVStride + 8 * (2 * slab + lg)]);
     };
     Frag8<T> kq[3][2];
 #pragma unroll
