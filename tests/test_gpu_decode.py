@@ -97,3 +97,50 @@ def test_decode_full_1m_sampled():
     wl = synth.WORKLOADS["full_decode_1m"]
     case = synth.workload_case(wl, seed=0, past_device="cuda")
     _run_and_check(case, seqs=[0, 3])
+
+
+def test_tiny_fp32_prefill_then_decode_against_oracle():
+    # The tiny workload as a serving run: prefill of the first 192 tokens,
+    # then 64 decode steps (sconv of the new token through the cached state,
+    # then split-K decode), every output row against the oracle's attention
+    # over the whole sequence.
+    import attention_sconv_amd as ink
+    wl = synth.WORKLOADS["tiny_fp32_swa_prefill"]
+    T, P, Hq, Hkv = 256, 192, 4, 1
+    case = synth.make_case("fp32", [T], [0], Hq, Hkv, wl.window, wl.bias_len, seed=0)
+    k_all, v_all, _ = oracle_sconv(case)
+    want, want_lse = oracle.relattn_prefill(case.q, k_all.reshape(T, Hkv, 128),
+                                            v_all.reshape(T, Hkv, 128), case.bias,
+                                            wl.window, Hq // Hkv)
+    gc = GpuCase(case, fill_nan=True)
+    d = gc.desc()
+    cu = torch.tensor([0, P], dtype=torch.int32, device="cuda")
+    sl = torch.tensor([P], dtype=torch.int32, device="cuda")
+    ink.inkattn_sconv(ink.FP32, Hkv, 128, 1, P, P, gc.k_pre[:P].contiguous(),
+                      gc.v_pre[:P].contiguous(), gc.conv_w, gc.conv_state, gc.state_slot, cu,
+                      gc.slot_mapping[:P].contiguous(), gc.k_cache, gc.v_cache)
+    o_p = torch.empty((P, Hq, 128), device="cuda")
+    l_p = torch.empty((P, Hq), device="cuda")
+    ink.inkattn_relattn_prefill(d, 1, P, P, gc.q[:P].contiguous(), gc.k_cache, gc.v_cache,
+                                gc.block_table, gc.block_table.shape[1], cu, sl, gc.bias, o_p,
+                                l_p)
+    outs, lses = [o_p], [l_p]
+    one = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    ws_bytes = ink.inkattn_relattn_decode_workspace_size(d, 1, T, 0)
+    ws = torch.empty(ws_bytes // 4 + 4, device="cuda")
+    for t in range(P, T):
+        ink.inkattn_sconv(ink.FP32, Hkv, 128, 1, 1, 1, gc.k_pre[t:t + 1].contiguous(),
+                          gc.v_pre[t:t + 1].contiguous(), gc.conv_w, gc.conv_state,
+                          gc.state_slot, one, gc.slot_mapping[t:t + 1].contiguous(),
+                          gc.k_cache, gc.v_cache)
+        L = torch.tensor([t + 1], dtype=torch.int32, device="cuda")
+        o = torch.empty((1, Hq, 128), device="cuda")
+        lse = torch.empty((1, Hq), device="cuda")
+        ink.inkattn_relattn_decode(d, 1, t + 1, gc.q[t:t + 1].contiguous(), gc.k_cache,
+                                   gc.v_cache, gc.block_table, gc.block_table.shape[1], L,
+                                   gc.bias, o, lse, 0, ws, ws_bytes)
+        outs.append(o)
+        lses.append(lse)
+    torch.cuda.synchronize()
+    assert_parity(host(torch.cat(outs)), want, "fp32", "prefill + decode outputs")
+    assert_parity(host(torch.cat(lses)), want_lse, "fp32", "prefill + decode lse")
