@@ -12,7 +12,7 @@ using inkattn::AttnShape;
 namespace {
 
 constexpr int kCUs = 256;                  // MI355X compute units
-constexpr int kDecodeTargetGroups = 2 * kCUs;     // (seq, kv-head, split) work-groups
+constexpr int kDecodeTargetGroups = kCUs;   // (seq, kv-head, split) work-groups, one per CU
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -149,6 +149,10 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       !aligned16(workspace))
     return INKATTN_EINVAL;
+  // The decode kernel addresses the bias table with 32-bit byte offsets.
+  const size_t elem = desc->dtype == INKATTN_BF16 ? 2 : 4;
+  if ((uint64_t)desc->num_q_heads * (uint64_t)desc->bias_len * elem >= (1ull << 31))
+    return INKATTN_ENOTSUP;
   const int32_t s = num_splits == 0 ? auto_splits(desc, num_seqs, max_seq_len) : num_splits;
   const size_t need = inkattn_relattn_decode_workspace_size(desc, num_seqs, max_seq_len, s);
   if (workspace_bytes < need) return INKATTN_EINVAL;

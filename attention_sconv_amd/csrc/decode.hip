@@ -8,12 +8,19 @@
 // per-configuration number of splits).  Logit of query head h at position
 // L-1 against key j:  q.k_j / sqrt(128) + bias[h][min(L-1-j, R-1)].
 //
-// Split kernel: one work-group of 4 waves per (split, kv-head, sequence).
-// The split owns a contiguous run of 128-token pages of the sequence's key
-// range; in every page wave w takes keys 32w .. 32w+31 and reads them straight
-// from HBM into MFMA operand registers (16 B per lane per load, next page
-// prefetched while the current one is computed), so the kernel streams each
-// K/V byte of the range exactly once.  All Hq/Hkv query heads of the group
+// Split kernel: one work-group of 8 waves per (split, kv-head, sequence),
+// sized to fill one compute unit (2 waves per SIMD).  The split owns a
+// contiguous run of 128-token pages of the sequence's key range, cut into
+// items of 32 keys (page, quarter) dealt round-robin: in round r wave w
+// takes item 8r + w.  The SIMD arbiter favours the older of its two waves;
+// left alone, the favoured waves would finish their share early and leave
+// the rest of the run at half occupancy, so the work-group meets at a
+// barrier every two rounds (no wave runs more than two items ahead, and the
+// order of every sum stays fixed: results are bitwise repeatable).  A wave
+// reads its item's K and V straight from HBM into MFMA operand registers
+// (16 B per lane per load, its next item prefetched while the current one is
+// computed, also across the barrier), so the kernel streams each K/V byte of
+// the range exactly once.  All Hq/Hkv query heads of the group
 // ride along in one 16-wide MFMA column tile:
 //   S^T[key][head] = K Q^T    (v_mfma 16x16x32, rows = keys, cols = heads)
 //   O^T[d][head]  += V^T P^T  (v_mfma 16x16x32, rows = dims,  cols = heads)
@@ -22,7 +29,7 @@
 // contiguous 16 B load.  Rows of the first product are ordered so that lane
 // group G ends up holding the probabilities of keys 8G .. 8G+7, exactly the
 // B-operand layout of the second product (no shuffles).
-// The four waves merge their running (max, sum, O) through LDS and write one
+// The eight waves merge their running (max, sum, O) through LDS and write one
 // normalised partial output and its log-sum-exp per (sequence, head, split).
 //
 // Merge kernel: per (sequence, q-head), lse = log sum_s exp(lse_s) and
@@ -34,11 +41,11 @@ namespace inkattn {
 
 namespace {
 
-constexpr int kDecodeWaves = 4;
+constexpr int kDecodeWaves = 8;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 
 template <typename T>
-__global__ __launch_bounds__(kDecodeThreads, 2) void decode_split_kernel(
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
     int Hq, int Hkv, int window, int R, int S, const T* __restrict__ q,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seq_lens,
@@ -53,7 +60,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_split_kernel(
   const int b = blockIdx.z;
   const int G = Hq / Hkv;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int col = lane & 15;      // MFMA column (query head in group) / row index for A loads
   const int grp = lane >> 4;      // lane group 0..3
 
@@ -65,6 +72,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_split_kernel(
   const int bps = (nblk + S - 1) / S;
   const int my_lo = blk_first + split * bps;
   const int my_hi = min(my_lo + bps, blk_last + 1);
+  const int n_items = 4 * max(my_hi - my_lo, 0);   // item i: page my_lo + i/4, keys 32(i%4) ..
 
   const bool head_ok = col < G;
   const int h = kvh * G + col;
@@ -73,7 +81,10 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_split_kernel(
   for (int ds = 0; ds < 4; ++ds)
     qf[ds] = head_ok ? Frag8<T>::load(q + ((size_t)b * Hq + h) * kHeadDim + 32 * ds + 8 * grp)
                      : Frag8<T>::zero();
-  const T* bias_h = bias + (size_t)(head_ok ? h : 0) * R;
+  // Bias row of this lane's head, as an element index into the whole table
+  // (the entry point keeps the table under 2 GiB).
+  const rsrc_t bias_r = make_rsrc(bias, (uint32_t)((size_t)Hq * R * sizeof(T)));
+  const uint32_t bias_row = (uint32_t)(head_ok ? h : 0) * (uint32_t)R;
 
   const float c = 0.08838834764831845f * kLog2e;   // log2(e) / sqrt(128)
   float m = -INFINITY;                             // running max (log2 units)
@@ -82,39 +93,48 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_split_kernel(
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0, 0, 0, 0};
 
-  // Row r of the S^T tile t is key 32w + 8*(r/4) + 4t + r%4, so accumulator
-  // register r of lane group G in tile t holds key 32w + 8G + 4t + r.
-  const int krow_base = 32 * wave + 8 * (col >> 2) + (col & 3);
-  const int key_lane = 32 * wave + 8 * grp;   // first of this lane's 8 keys in the page
-
   auto page_base = [&](int blk) -> size_t {
     const int phys = block_table[(size_t)b * max_blocks + blk];
     return ((size_t)phys * Hkv + kvh) * (size_t)(kPage * kHeadDim);
   };
-  // Everything a page needs is loaded in one batch, one page ahead: K and V^T
-  // fragments and the 8 bias entries of this lane's keys.  Bias indices are
-  // clamped into the table (masked keys are dropped later by a select), so
-  // no load sits behind a branch and no wait drains the prefetch.
-  auto load_page = [&](int blk, Frag8<T>* kf, Frag8<T>* vf, T* bb) {
-    const int j0 = blk * kPage + key_lane;
+  // Row r of the S^T tile t of item (page, u) is key 32u + 8*(r/4) + 4t + r%4
+  // of the page, so accumulator register r of lane group G in tile t holds
+  // key 32u + 8G + 4t + r.
+  // Everything an item needs is loaded in one batch, one item ahead: K and
+  // V^T fragments and the 8 bias entries of this lane's keys.  Bias indices
+  // are clamped into the table (masked keys are dropped later by a select),
+  // so no load sits behind a branch and no wait drains the prefetch.
+  // Each page is read through a buffer descriptor of its own; the quarter
+  // and the dim tile are wave-uniform offsets, so the only per-lane address
+  // state is one fixed byte offset for K and one for V^T.
+  constexpr uint32_t kPageBytes = kPage * kHeadDim * sizeof(T);
+  const uint32_t k_lane = ((8 * (col >> 2) + (col & 3)) * kHeadDim + 8 * grp) * sizeof(T);
+  const uint32_t v_lane = (col * kPage + 8 * grp) * sizeof(T);
+  auto load_item = [&](int item, Frag8<T>* kf, Frag8<T>* vf, T* bb) {
+    const int blk = my_lo + (item >> 2);
+    const int u = item & 3;
+    const int j0 = blk * kPage + 32 * u + 8 * grp;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bb[e] = bias_h[min(max(L - 1 - (j0 + e), 0), R - 1)];
+    for (int e = 0; e < 8; ++e)
+      bb[e] = buf_load_elem<T>(bias_r, (bias_row + min(max(L - 1 - (j0 + e), 0), R - 1)) * sizeof(T));
     const size_t base = page_base(blk);
-    const T* kt = k_cache + base;
-    const T* vt = v_cache + base;
+    const rsrc_t kr = make_rsrc(k_cache + base, kPageBytes);
+    const rsrc_t vr = make_rsrc(v_cache + base, kPageBytes);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds)
-        kf[t * 4 + ds] = Frag8<T>::load(kt + (size_t)(krow_base + 4 * t) * kHeadDim + 32 * ds + 8 * grp);
+        kf[t * 4 + ds] = Frag8<T>::load(kr, k_lane + (4 * t * kHeadDim + 32 * ds) * sizeof(T),
+                                        32 * u * kHeadDim * sizeof(T));
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-      vf[dt] = Frag8<T>::load(vt + (size_t)(16 * dt + col) * kPage + key_lane);
+      vf[dt] = Frag8<T>::load(vr, v_lane, (32 * u + 16 * dt * kPage) * sizeof(T));
   };
 
-  // One page of this wave's 32 keys: scores, online softmax, O^T += V^T P^T.
-  auto process_page = [&](int blk, const Frag8<T>* kf, Frag8<T>* vf, const T* bb) {
-    const int j0 = blk * kPage + key_lane;
+  // One item of 32 keys: scores, online softmax, O^T += V^T P^T.
+  auto process_item = [&](int item, const Frag8<T>* kf, Frag8<T>* vf, const T* bb) {
+    const int blk = my_lo + (item >> 2);
+    const int j0 = blk * kPage + 32 * (item & 3) + 8 * grp;
     f32x4 sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -155,7 +175,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_split_kernel(
     // per-lane part is a select, never a divergent branch around the MFMA
     // (matrix instructions must run with every lane active).
     if (blk == blk_last && (L & (kPage - 1)) != 0) {
-      const int nvalid = L - (blk * kPage + key_lane);
+      const int nvalid = L - j0;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) vf[dt] = vf[dt].keep_first(nvalid);
     }
@@ -163,24 +183,38 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_split_kernel(
     for (int dt = 0; dt < 8; ++dt) o[dt] = mfma16(vf[dt], pf, o[dt]);
   };
 
-  // Pages alternate between two register sets, so the next page's loads are
-  // in flight while the current one is computed and no register copy (which
-  // would wait for those loads) is needed between iterations.
-  // Loads are unconditional (a page index past the split re-reads the
-  // split's last page, an L2 hit) so the memory-wait bookkeeping stays exact
-  // and each page only waits for its own loads.
+  // A wave's items alternate between two register sets, so the next item's
+  // loads are in flight while the current one is computed and no register
+  // copy (which would wait for those loads) is needed between rounds.
+  // Inside the main loop every load is unconditional (a wave without an item
+  // in the last round re-reads the split's last item, an L2 hit) so the
+  // memory-wait bookkeeping stays exact and each item only waits for its own
+  // loads; the last one or two rounds are peeled so that no load is issued
+  // for a round that does not exist.  The barrier carries no memory fence:
+  // it only holds waves together, it does not wait for their loads.
   Frag8<T> ka[8], va[8], kb[8], vb[8];
   T ba[8], bbb[8];
-  const int last = my_hi - 1;
-  if (my_lo < my_hi) load_page(my_lo, ka, va, ba);
-  for (int blk = my_lo; blk < my_hi; blk += 2) {
-    load_page(min(blk + 1, last), kb, vb, bbb);
-    process_page(blk, ka, va, ba);
-    load_page(min(blk + 2, last), ka, va, ba);
-    if (blk + 1 < my_hi) process_page(blk + 1, kb, vb, bbb);
+  const int rounds = (n_items + kDecodeWaves - 1) / kDecodeWaves;
+  auto item_of = [&](int r) { return min(r * kDecodeWaves + wave, n_items - 1); };
+  auto has_item = [&](int r) { return r * kDecodeWaves + wave < n_items; };
+  if (rounds > 0) load_item(item_of(0), ka, va, ba);
+  int r = 0;
+  for (; r + 2 < rounds; r += 2) {
+    load_item(item_of(r + 1), kb, vb, bbb);
+    process_item(item_of(r), ka, va, ba);      // rounds before the last are full
+    load_item(item_of(r + 2), ka, va, ba);
+    process_item(item_of(r + 1), kb, vb, bbb);
+    __builtin_amdgcn_s_barrier();
+  }
+  if (r + 1 < rounds) {
+    load_item(item_of(r + 1), kb, vb, bbb);
+    process_item(item_of(r), ka, va, ba);
+    if (has_item(r + 1)) process_item(item_of(r + 1), kb, vb, bbb);
+  } else if (r < rounds && has_item(r)) {
+    process_item(item_of(r), ka, va, ba);
   }
 
-  // Merge the four waves.  O^T register r of tile dt is dim 16dt + 4G + r.
+  // Merge the eight waves.  O^T register r of tile dt is dim 16dt + 4G + r.
   float lt = l + wave_shfl_xor(l, 16);
   lt = pair_sum(lt);
   if (grp == 0) {

@@ -57,6 +57,28 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
   return bf16{f32_to_bf16_bits(x)};
 }
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer descriptor (gfx9 family): base address and byte count held in
+// four scalar registers.  A load adds a 32-bit per-lane byte offset and a
+// wave-uniform byte offset to the base, so wave-uniform address parts stay
+// out of vector registers.  Word 3 selects untyped access with no swizzle.
+// Reads past the byte count return zero rather than faulting.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+template <typename T> __device__ __forceinline__ T buf_load_elem(rsrc_t r, uint32_t voff);
+template <> __device__ __forceinline__ bf16 buf_load_elem<bf16>(rsrc_t r, uint32_t voff) {
+  return bf16{__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0))};
+}
+template <> __device__ __forceinline__ float buf_load_elem<float>(rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+
 // ---------------------------------------------------------------- frag8
 template <typename T> struct Frag8;
 
@@ -64,6 +86,9 @@ template <> struct Frag8<bf16> {
   u32x4 v;                                   // 8 bf16, element e in bits 16*(e%2) of word e/2
   __device__ __forceinline__ static Frag8 load(const bf16* p) {
     Frag8 f; f.v = *reinterpret_cast<const u32x4*>(p); return f;
+  }
+  __device__ __forceinline__ static Frag8 load(rsrc_t r, uint32_t voff, uint32_t soff) {
+    Frag8 f; f.v = buf_load16(r, voff, soff); return f;
   }
   __device__ __forceinline__ void store(bf16* p) const {
     *reinterpret_cast<u32x4*>(p) = v;
@@ -117,6 +142,12 @@ template <> struct Frag8<float> {
     Frag8 f;
     f.lo = *reinterpret_cast<const f32x4*>(p);
     f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+    return f;
+  }
+  __device__ __forceinline__ static Frag8 load(rsrc_t r, uint32_t voff, uint32_t soff) {
+    Frag8 f;
+    f.lo = __builtin_bit_cast(f32x4, buf_load16(r, voff, soff));
+    f.hi = __builtin_bit_cast(f32x4, buf_load16(r, voff + 16, soff));
     return f;
   }
   __device__ __forceinline__ void store(float* p) const {

@@ -147,14 +147,16 @@ size_t inkattn_relattn_decode_workspace_size(const inkattn_attn_desc_t* desc,
  * Same logits as inkattn_relattn_prefill.  Split-K: each (sequence, kv-head,
  * split) work-group attends over its share of the key blocks with all
  * Hq/Hkv query heads of the group, writes a partial output and
- * log-sum-exp to `workspace`, and a second kernel merges the splits.
+ * log-sum-exp to `workspace`, and a second kernel merges the splits (with
+ * one split the work-group writes out/lse itself and no merge runs).
  *
  *   q     [num_seqs][Hq][128]
  *   out   [num_seqs][Hq][128], lse float [num_seqs][Hq] or NULL
  *   max_seq_len: host upper bound of seq_lens[b].
  *   num_splits : 0 = auto (inkattn_relattn_decode_num_splits), else >= 1.
  *   workspace  : device memory of at least
- *                inkattn_relattn_decode_workspace_size(...) bytes, 16 B aligned. */
+ *                inkattn_relattn_decode_workspace_size(...) bytes, 16 B aligned.
+ * INKATTN_ENOTSUP if the bias table (Hq * R elements) reaches 2 GiB. */
 inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t num_seqs,
                                         int32_t max_seq_len, const void* q,
                                         const void* k_cache, const void* v_cache,

@@ -130,11 +130,25 @@ def test_decode_workspace_rules():
 
 
 def test_num_splits_heuristic():
-    # enough (seq, kv-head, split) groups for 2 per compute unit, never more
-    # splits than pages in the attended range
+    # enough (seq, kv-head, split) work-groups for one per compute unit, never
+    # more splits than pages in the attended range
     sw = _desc(W=4096, R=4096)
-    assert ink.inkattn_relattn_decode_num_splits(sw, 64, 16384) == 2
+    assert ink.inkattn_relattn_decode_num_splits(sw, 64, 16384) == 1
+    assert ink.inkattn_relattn_decode_num_splits(sw, 16, 16384) == 4
     full = _desc(W=0, R=1 << 20)
-    assert ink.inkattn_relattn_decode_num_splits(full, 4, 1 << 20) == 32
+    assert ink.inkattn_relattn_decode_num_splits(full, 4, 1 << 20) == 16
     assert ink.inkattn_relattn_decode_num_splits(full, 1, 100) == 1
     assert ink.inkattn_relattn_decode_num_splits(full, 1, 300) == 3
+
+
+def test_decode_rejects_bias_table_of_2gib():
+    # the decode kernel addresses the [Hq][R] bias table with 32-bit byte offsets
+    lib = ink._lib._lib
+    big = _desc(dtype=1, Hq=32, R=1 << 25)            # 32 * 2^25 * 2 B = 2 GiB
+    st = lib.inkattn_relattn_decode(ctypes.byref(big), 1, 100, FAKE, FAKE, FAKE, FAKE, 1, FAKE,
+                                    FAKE, FAKE, None, 0, FAKE, 1 << 30, None)
+    assert st == ink.ENOTSUP
+    big32 = _desc(dtype=0, Hq=32, R=1 << 24)          # fp32: 32 * 2^24 * 4 B = 2 GiB
+    st = lib.inkattn_relattn_decode(ctypes.byref(big32), 1, 100, FAKE, FAKE, FAKE, FAKE, 1,
+                                    FAKE, FAKE, FAKE, None, 0, FAKE, 1 << 30, None)
+    assert st == ink.ENOTSUP
