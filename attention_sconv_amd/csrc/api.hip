@@ -51,6 +51,12 @@ int32_t auto_splits(const inkattn_attn_desc_t* d, int32_t num_seqs, int32_t max_
   return (int32_t)s;
 }
 
+// The kernels address the [Hq][R] bias table with 32-bit byte offsets.
+bool bias_table_too_large(const inkattn_attn_desc_t* d) {
+  const uint64_t elem = d->dtype == INKATTN_BF16 ? 2 : 4;
+  return (uint64_t)d->num_q_heads * (uint64_t)d->bias_len * elem >= (1ull << 31);
+}
+
 inkattn_status_t from_hip(hipError_t e) { return e == hipSuccess ? INKATTN_OK : INKATTN_EHIP; }
 
 }  // namespace
@@ -109,6 +115,7 @@ inkattn_status_t inkattn_relattn_prefill(const inkattn_attn_desc_t* desc, int32_
     return INKATTN_EINVAL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return INKATTN_EINVAL;
+  if (bias_table_too_large(desc)) return INKATTN_ENOTSUP;
   return from_hip(inkattn::launch_prefill(shape_of(desc), num_seqs, max_q_len, q, k_cache,
                                           v_cache, block_table, max_blocks_per_seq,
                                           cu_seqlens_q, seq_lens, bias, out, lse,
@@ -149,10 +156,7 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       !aligned16(workspace))
     return INKATTN_EINVAL;
-  // The decode kernel addresses the bias table with 32-bit byte offsets.
-  const size_t elem = desc->dtype == INKATTN_BF16 ? 2 : 4;
-  if ((uint64_t)desc->num_q_heads * (uint64_t)desc->bias_len * elem >= (1ull << 31))
-    return INKATTN_ENOTSUP;
+  if (bias_table_too_large(desc)) return INKATTN_ENOTSUP;
   const int32_t s = num_splits == 0 ? auto_splits(desc, num_seqs, max_seq_len) : num_splits;
   const size_t need = inkattn_relattn_decode_workspace_size(desc, num_seqs, max_seq_len, s);
   if (workspace_bytes < need) return INKATTN_EINVAL;

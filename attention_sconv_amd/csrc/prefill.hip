@@ -13,10 +13,15 @@
 //   v_mfma_f32_32x32x2_f32 on the same fragments).  Wave w owns query rows
 //   32w .. 32w+31 as the 32 MFMA columns, so every softmax row statistic is
 //   one lane plus its partner 32 lanes away.
-// * K and V^T tiles of 64 keys are staged global -> registers -> LDS in
-//   padded rows (conflict-free fragment reads at fixed offsets),
-//   double-buffered with one barrier per tile; the next tile's loads are in
-//   flight while the current tile is computed.
+// * Ping-pong phases: a wave alternates matrix phases (QK^T of tile i with
+//   the PV of tile i-1) and softmax phases (tile i).  Waves 4-7 run one phase
+//   behind waves 0-3 and a barrier closes every phase, so the two waves that
+//   share a SIMD are always in opposite phases and the matrix cores and the
+//   vector ALU work at the same time.
+// * K and V^T tiles of 64 keys go global -> LDS by buffer loads with the
+//   LDS-DMA flag (no staging registers) into padded rows (conflict-free
+//   fragment reads at fixed offsets), double-buffered; a tile's loads have
+//   two phases to land.
 // * Sheared bias: for a (256-query, 64-key) tile the relative distances form
 //   a band of 319 values.  The band, pre-multiplied by sqrt(128) and holding
 //   -inf where the key is outside the causal window, is written to LDS once
@@ -51,10 +56,8 @@ constexpr int kBand = kBQ + kBK - 1;     // 319 distinct distances per tile
 // (4 copies x 4 consecutive 16-byte groups) hit 16 distinct bank groups.
 constexpr int kBandPad = 336;
 static_assert(kBandPad >= kBand + 1 && kBandPad % 64 == 16, "band copy stride");
-constexpr int kStageFrags = kBK * kHeadDim / 8 / kThreads;   // fragments per thread per tile
 constexpr int kXcds = 8;
 constexpr float kRescaleSlack = 8.0f;    // log2 units
-static_assert(kStageFrags * kThreads * 8 == kBK * kHeadDim, "staging covers one tile");
 static_assert((kBQ - 1) % 4 == 3, "band copy selection assumes kBQ % 4 == 0");
 static_assert(kBand <= kThreads, "one band entry per thread");
 
@@ -68,11 +71,22 @@ static_assert(kBand <= kThreads, "one band entry per thread");
 constexpr int kKStride = kHeadDim + 8;   // elements per K row in LDS
 constexpr int kVStride = kBK + 8;        // elements per V^T row in LDS
 
+// Raw bias slice of one stage: the kBand distances of a tile, fetched as
+// whole dwords (from a dword-aligned start) by whole wave loads.
+template <typename T>
+constexpr int band_raw_dwords() {
+  constexpr int epd = 4 / (int)sizeof(T);                       // elements per dword
+  constexpr int dwords = (kBand + epd - 1 + epd - 1) / epd;     // + alignment slack
+  return (dwords + 63) / 64 * 64;
+}
+
 template <typename T>
 struct PrefillSmem {
   T k[2][kBK * kKStride];                // [key][d]
   T vt[2][kHeadDim * kVStride];          // [d][key]
   float band[2][4][kBandPad];            // copy s holds band[v + s]
+  uint32_t braw[2][band_raw_dwords<T>()];  // raw bias slice of a stage
+  int32_t pages[2][2];                   // physical pages of a stage's K and V tiles
 };
 
 struct PrefillArgs {
@@ -97,11 +111,50 @@ __device__ __forceinline__ int keyperm(int r) {
   return 16 * (a >> 1) + 8 * g + 4 * (a & 1) + c;
 }
 
-template <typename T>
-struct Stage {
-  Frag8<T> k[kStageFrags], v[kStageFrags];
-  float band;
-};
+// Raw buffer descriptor (gfx9 family) of `bytes` bytes at p, in scalar
+// registers (p and bytes must be wave-uniform).  Word 3 selects untyped
+// access; reads past `bytes` return zero.
+__device__ __forceinline__ u32x4 make_buf_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu),
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+// One 16-byte buffer load straight into LDS: lane l writes its 16 bytes at
+// LDS byte address lds + 16 l (M0 holds lds; it is set here and used by
+// nothing else in these kernels).  rsrc is a raw buffer descriptor, voff the
+// lane's byte offset, soff a wave-uniform byte offset.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+// An empty asm that reads a fragment: forces its load to have completed here.
+__device__ __forceinline__ void keep_live(const Frag8<bf16>& f) { asm volatile("" :: "v"(f.v)); }
+__device__ __forceinline__ void keep_live(const Frag8<float>& f) {
+  asm volatile("" :: "v"(f.lo), "v"(f.hi));
+}
+__device__ __forceinline__ void keep_live(int x) { asm volatile("" :: "v"(x)); }
+__device__ __forceinline__ void keep_live(float x) { asm volatile("" :: "v"(x)); }
+__device__ __forceinline__ void keep_live(bf16 x) { asm volatile("" :: "v"(x.bits)); }
+// One 4-byte buffer load straight into LDS: lane l writes at lds + 4 l.
+__device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+// Wait until every load this wave issued (including the LDS-DMA ones) landed.
+__device__ __forceinline__ void wait_all_loads() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+// Keep the first n elements of a 16-byte slot of T, zero the rest.
+template <typename T> __device__ __forceinline__ u32x4 keep_first_elems(u32x4 v, int n);
+template <> __device__ __forceinline__ u32x4 keep_first_elems<bf16>(u32x4 v, int n) {
+  Frag8<bf16> f; f.v = v; return f.keep_first(n).v;
+}
+template <> __device__ __forceinline__ u32x4 keep_first_elems<float>(u32x4 v, int n) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = e < n ? v[e] : 0u;
+  return v;
+}
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
@@ -131,10 +184,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   const int key_lo = A.window > 0 ? max(0, P0 - A.window + 1) : 0;
   const int jt_lo = key_lo / kBK;
   const int jt_hi = P_last / kBK;
+  const int n_t = jt_hi - jt_lo + 1;                       // KV tiles visited (>= 1)
+  const int n_tail = seq_len - jt_hi * kBK;                // valid keys of the last tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave >> 2;        // 0: waves 0-3; 1: waves 4-7, one phase behind
   const int lq = lane & 31;          // query column within the wave
   const int lg = lane >> 5;          // lane group (k-half)
   const int a_row = 32 * wave + lq;  // query row within the tile
@@ -152,46 +208,188 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
     const T* qrow = qp + ((size_t)(tok0 + row0 + a_row) * A.Hq + h) * kHeadDim + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = row_ok ? Frag8<T>::load(qrow + 16 * ks) : Frag8<T>::zero();
+    // Consume the fragments here, so that the compiler's own memory-wait
+    // bookkeeping sees these loads finished before the phase loop and never
+    // waits there (such a wait would also stall on the in-flight tile loads,
+    // which the bookkeeping cannot see).
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) keep_live(qf[ks]);
   }
 
   const float sqrt_d = 11.313708498984761f;               // sqrt(128)
   const float c = kLog2e / sqrt_d;
 
-  // ---- staging of one KV tile
-  auto stage_load = [&](int jt, Stage<T>& s) {
-    const int J0 = jt * kBK;
-    const int phys = btab[J0 / kPage];
-    const int koff = J0 % kPage;
-    const size_t tile = ((size_t)phys * A.Hkv + kvg) * (size_t)(kPage * kHeadDim);
-    // The whole 64-key slice lies inside one allocated page, so every load is
-    // in bounds (keys >= seq_len of the last tile are cleaned up in LDS).
+  // ---- staging.  Stage s holds K and the bias band of tile s and V of tile
+  // s-1 (stage n_t holds only V of the last tile): V is consumed one tile
+  // after K.  Every per-stage read of global memory is a buffer load with
+  // the LDS-DMA flag (lane l of a wave's load writes its bytes at slot l of
+  // the destination): K and V^T tiles, the raw bias slice and the block-table
+  // entries.  No register holds them and the compiler's memory-wait
+  // bookkeeping never sees them (it would otherwise wait for them before LDS
+  // reads it cannot tell apart, or at loop back edges); they are written as
+  // inline assembly and waited for explicitly:
+  //   * stage s+1's tiles are issued right after the barrier that closes
+  //     phase 2s-1 (their buffers held tiles s-1 and s-2, which nobody reads
+  //     any more) and waited for at the end of phase 2s+1, before the barrier
+  //     that publishes them: two phases to land;
+  //   * the bias slice and the block-table entries of a stage travel one
+  //     stage earlier still, so that they are published by a barrier before
+  //     other waves read them (the band conversion reads entries fetched by
+  //     other waves; the tile loads of a stage need its page numbers).
+  // Each lane fetches whichever (row, chunk) the padded tile layout keeps at
+  // its slot; padding slots receive a harmless copy.  Keys >= seq_len exist
+  // only in the sequence's last tile and hold no data (possibly NaN); once a
+  // wave's loads have landed it zeroes those K rows and V^T columns in its
+  // own slots, so 0 * garbage cannot reach O and masked logits stay -inf
+  // rather than NaN.
+  constexpr int kSlotBytes = 16;
+  constexpr int kKRowSlots = kKStride * (int)sizeof(T) / kSlotBytes;    // incl. padding
+  constexpr int kKDataSlots = kHeadDim * (int)sizeof(T) / kSlotBytes;
+  constexpr int kKLoads = kBK * kKRowSlots / 64;                        // wave loads per K tile
+  constexpr int kVRowSlots = kVStride * (int)sizeof(T) / kSlotBytes;
+  constexpr int kVDataSlots = kBK * (int)sizeof(T) / kSlotBytes;
+  constexpr int kVLoads = kHeadDim * kVRowSlots / 64;
+  // Tile loads are issued by waves 4-7 only (at the start of their softmax
+  // phase); waves 0-3 go straight from the barrier into their matrix phase.
+  constexpr int kLoaders = kWaves / 2;
+  const int lw = wave - kLoaders;                                       // loader index (>= 0 for waves 4-7)
+  constexpr int kKPer = (kKLoads + kLoaders - 1) / kLoaders;
+  constexpr int kVPer = (kVLoads + kLoaders - 1) / kLoaders;
+  constexpr int kEpd = 4 / (int)sizeof(T);                              // bias elements per dword
+  constexpr int kBandLoads = band_raw_dwords<T>() / 64;
+  static_assert(kBK * kKRowSlots % 64 == 0 && kHeadDim * kVRowSlots % 64 == 0,
+                "tile buffers are whole wave loads");
+  constexpr int kBandPer = (kBandLoads + kLoaders - 1) / kLoaders;
+  constexpr uint32_t kPageBytes = kPage * kHeadDim * sizeof(T);
+
+  const uint32_t bias_bytes = (uint32_t)A.Hq * (uint32_t)A.R * sizeof(T);
+  const u32x4 bias_rsrc = make_buf_rsrc(A.bias, bias_bytes);
+  const u32x4 btab_rsrc = make_buf_rsrc(btab, (uint32_t)A.max_blocks * 4u);
+  auto page_rsrc = [&](const T* cache, int phys) {
+    return make_buf_rsrc(cache + ((size_t)phys * A.Hkv + kvg) * (size_t)(kPage * kHeadDim),
+                         kPageBytes);
+  };
+  auto lds_addr = [](const void* p) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
+  };
+  // First element (absolute, dword-aligned) of the bias slice of stage x.
+  auto band_e0 = [&](int x) {
+    const int d_lo = P0 - (jt_lo + x) * kBK - kBK + 1;          // smallest distance of the band
+    const int e0 = h * A.R + d_lo;
+    return e0 - (((e0 % kEpd) + kEpd) % kEpd);
+  };
+  // Slice of stage x and the block-table entries of stage x (one stage ahead).
+  auto dma_ahead = [&](int x) {
+    if (lw < 0) return;                           // only waves 4-7 load
+    const int ln = lane;
+    if (x < n_t) {
 #pragma unroll
-    for (int p = 0; p < kStageFrags; ++p) {
-      const int F = tid + kThreads * p;
-      const int r = F >> 4, f = F & 15;                   // K: 64 rows x 16 fragments
-      s.k[p] = Frag8<T>::load(kc + tile + (size_t)(koff + r) * kHeadDim + 8 * f);
-      const int d = F >> 3, fv = F & 7;                   // V^T: 128 rows x 8 fragments
-      s.v[p] = Frag8<T>::load(vc + tile + (size_t)d * kPage + koff + 8 * fv);
+      for (int j = 0; j < kBandPer; ++j) {
+        const int n = lw + kLoaders * j;
+        if (n < kBandLoads) {
+          const uint32_t voff = (uint32_t)(band_e0(x) * (int)sizeof(T)) + 4u * (64 * n + ln);
+          lds_dma4(bias_rsrc, lds_addr(&sm.braw[x & 1][64 * n]), voff, 0u);
+        }
+      }
     }
-    if (tid < kBand) {
-      const int dist = P0 - J0 + (kBQ - 1) - tid;
-      const bool vis = dist >= 0 && (A.window == 0 || dist < A.window);
-      s.band = vis ? to_f32(bias_h[min(dist, A.R - 1)]) * sqrt_d : -INFINITY;
+    if (x <= n_t && wave == kWaves - 1 && ln < 2) {
+      const int jt = min(max(jt_lo + x - ln, jt_lo), jt_hi);    // lane 0: K tile x, lane 1: V tile x-1
+      lds_dma4(btab_rsrc, lds_addr(&sm.pages[x & 1][0]), (uint32_t)(jt * kBK / kPage) * 4u, 0u);
     }
   };
-  auto stage_store = [&](int buf, const Stage<T>& s) {
+  // Tile loads of stage x, on page numbers published earlier.
+  auto dma_tiles = [&](int x, int k_phys, int v_phys) {
+    if (lw < 0) return;                           // only waves 4-7 load
+    const int ln = lane;                          // (per-lane offsets are loop-invariant)
+    if (x < n_t) {                                   // K of tile x
+      const int jt = jt_lo + x;
+      const u32x4 r = page_rsrc(kc, k_phys);
+      const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(jt * kBK % kPage) * kHeadDim * sizeof(T));
+      const uint32_t lds = lds_addr(&sm.k[x & 1][0]);
 #pragma unroll
-    for (int p = 0; p < kStageFrags; ++p) {
-      const int F = tid + kThreads * p;
-      const int r = F >> 4, f = F & 15;
-      s.k[p].store(&sm.k[buf][r * kKStride + 8 * f]);
-      const int d = F >> 3, fv = F & 7;
-      s.v[p].store(&sm.vt[buf][d * kVStride + 8 * fv]);
+      for (int j = 0; j < kKPer; ++j) {
+        const int n = lw + kLoaders * j;
+        if (n < kKLoads) {
+          const int slot = 64 * n + ln;
+          const int row = slot / kKRowSlots, ch = min(slot % kKRowSlots, kKDataSlots - 1);
+          lds_dma16(r, lds + 1024u * n, (uint32_t)(row * kHeadDim * (int)sizeof(T) + ch * kSlotBytes), soff);
+        }
+      }
     }
-    if (tid < kBand) {
+    if (x >= 1) {                                    // V of tile x-1
+      const int jt = jt_lo + x - 1;
+      const u32x4 r = page_rsrc(vc, v_phys);
+      const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(jt * kBK % kPage) * sizeof(T));
+      const uint32_t lds = lds_addr(&sm.vt[(x - 1) & 1][0]);
 #pragma unroll
-      for (int sh = 0; sh < 4; ++sh)
-        if (tid - sh >= 0) sm.band[buf][sh][tid - sh] = s.band;
+      for (int j = 0; j < kVPer; ++j) {
+        const int n = lw + kLoaders * j;
+        if (n < kVLoads) {
+          const int slot = 64 * n + ln;
+          const int row = slot / kVRowSlots, ch = min(slot % kVRowSlots, kVDataSlots - 1);
+          lds_dma16(r, lds + 1024u * n, (uint32_t)(row * kPage * (int)sizeof(T) + ch * kSlotBytes), soff);
+        }
+      }
+    }
+  };
+  auto stage_pages = [&](int x, int& k_phys, int& v_phys) {   // published by a barrier
+    k_phys = __builtin_amdgcn_readfirstlane(sm.pages[x & 1][0]);
+    v_phys = __builtin_amdgcn_readfirstlane(sm.pages[x & 1][1]);
+  };
+  auto fix_tail = [&](int x) {                       // after this wave's loads landed
+    if (lw < 0 || n_tail >= kBK) return;             // the slots of waves 4-7 only
+    // An opaque copy of the lane index keeps this once-per-work-group
+    // arithmetic here instead of being hoisted out of the phase loop (where
+    // its results would hold registers for the whole loop).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if (x < n_t && jt_lo + x == jt_hi) {
+      char* buf = reinterpret_cast<char*>(&sm.k[x & 1][0]);
+#pragma unroll
+      for (int j = 0; j < kKPer; ++j) {
+        const int n = lw + kLoaders * j;
+        const int slot = 64 * n + ln;
+        if (n < kKLoads && slot / kKRowSlots >= n_tail)
+          *reinterpret_cast<u32x4*>(buf + kSlotBytes * slot) = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (x >= 1 && jt_lo + x - 1 == jt_hi) {
+      char* buf = reinterpret_cast<char*>(&sm.vt[(x - 1) & 1][0]);
+      constexpr int kPer = kSlotBytes / (int)sizeof(T);          // keys per 16-byte slot
+#pragma unroll
+      for (int j = 0; j < kVPer; ++j) {
+        const int n = lw + kLoaders * j;
+        const int slot = 64 * n + ln;
+        const int ch = slot % kVRowSlots;
+        if (n < kVLoads && ch < kVDataSlots && kPer * (ch + 1) > n_tail) {
+          u32x4* q16 = reinterpret_cast<u32x4*>(buf + kSlotBytes * slot);
+          *q16 = keep_first_elems<T>(*q16, n_tail - kPer * ch);
+        }
+      }
+    }
+  };
+  // Bias band of stage x from its raw slice (published by an earlier
+  // barrier): pre-multiplied by sqrt(128), -inf outside the causal window,
+  // distances >= R take bias[R-1].  Four copies shifted by one entry.
+  const float bias_last = to_f32(bias_h[A.R - 1]);
+  keep_live(bias_last);
+  // Written by waves 0-3 (256 threads), at the end of their softmax phase.
+  auto band_store = [&](int x) {
+    if (x >= n_t) return;
+    const T* raw = reinterpret_cast<const T*>(&sm.braw[x & 1][0]);
+    const int e0 = band_e0(x);
+#pragma unroll
+    for (int k = 0; k < (kBand + kThreads / 2 - 1) / (kThreads / 2); ++k) {
+      const int v = tid + (kThreads / 2) * k;
+      if (v < kBand) {
+        const int dist = P0 - (jt_lo + x) * kBK + (kBQ - 1) - v;
+        const bool vis = dist >= 0 && (A.window == 0 || dist < A.window);
+        const float bv = dist > A.R - 1 ? bias_last : to_f32(raw[h * A.R + dist - e0]);
+        const float band_v = vis ? bv * sqrt_d : -INFINITY;
+#pragma unroll
+        for (int sh = 0; sh < 4; ++sh)
+          if (v - sh >= 0) sm.band[x & 1][sh][v - sh] = band_v;
+      }
     }
   };
 
@@ -203,95 +401,95 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
+  f32x16 acc[2];           // S^T of the tile between its matrix and softmax phases
+  bool rescale = false;    // the last softmax phase moved the running max ...
+  float alpha = 1.0f;      // ... and O must be scaled by alpha before its P V
+  Frag8<T> pf[4];          // P^T of the tile between its softmax and the next matrix phase
 
   const int kp = keyperm(lq);
   const int band_shift = (3 - (lane & 3)) & 3;
 
-  Stage<T> st;
-  stage_load(jt_lo, st);
-  stage_store(0, st);
-  __syncthreads();
-
-  // Keys >= seq_len exist only in the sequence's last tile.  They hold no
-  // data (possibly NaN), so before that tile is used its K rows and V^T
-  // columns past seq_len are zeroed in LDS: 0 * garbage must not reach O,
-  // and the masked logits must stay -inf rather than NaN.
-  const int n_tail = seq_len - jt_hi * kBK;               // valid keys of the last tile
-  auto clean_tail = [&](int buf) {
+  // Matrix phase of tile i: S^T_i = K_i Q^T (accumulators start as the
+  // sheared bias band) and O^T += V^T_{i-1} P^T_{i-1}, interleaved two + two
+  // MFMAs per k-step.  Every matrix phase runs both products, which keeps one
+  // copy of the code: in the first, P^T is zero and V buffer 1 has been
+  // zeroed, so O gains exactly +0; the closing phase (i = n_t) computes a
+  // QK^T from whatever finite or stale data buffer n_t % 2 holds and nothing
+  // reads it.
+  // LDS fragment reads run ahead of the MFMAs that consume them (K two
+  // k-steps ahead, V one) and sched_barrier keeps the compiler from sinking
+  // them back next to their uses.
+  auto matrix_phase = [&](int i) {
+    constexpr bool kQK = true, kPV = true;
+    const int kb = i & 1, vb = (i - 1) & 1;
+    auto kfrag = [&](int ks, int t) {
+      return Frag8<T>::load(&sm.k[kb][(32 * t + kp) * kKStride + 8 * (2 * ks + lg)]);
+    };
+    auto vfrag = [&](int step, int j) {          // k-step `step` uses slab step/2, dims tile 2(step%2)+j
+      const int dr = 32 * (2 * (step & 1) + j) + lq;
+      return Frag8<T>::load(&sm.vt[vb][dr * kVStride + 8 * (2 * (step >> 1) + lg)]);
+    };
+    Frag8<T> kq[3][2], vq[2][2];
+    if constexpr (kQK) {
 #pragma unroll
-    for (int p = 0; p < kStageFrags; ++p) {
-      const int F = tid + kThreads * p;
-      const int r = F >> 4, f = F & 15;
-      if (r >= n_tail) Frag8<T>::zero().store(&sm.k[buf][r * kKStride + 8 * f]);
-      const int d = F >> 3, fv = F & 7;
-      if (8 * fv + 8 > n_tail) {
-        T* q8 = &sm.vt[buf][d * kVStride + 8 * fv];
-        Frag8<T>::load(q8).keep_first(n_tail - 8 * fv).store(q8);
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) kq[j][t] = kfrag(j, t);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int v0 = (kBQ - 1) - a_row + 32 * t + 16 * hh + 8 * lg;
+          const float* bp = &sm.band[kb][band_shift][v0 - band_shift];
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(bp);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(bp + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[t][8 * hh + e] = x0[e];
+            acc[t][8 * hh + 4 + e] = x1[e];
+          }
+        }
+    }
+    if constexpr (kPV) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) vq[0][j] = vfrag(0, j);
+      if (rescale) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) asm("v_mul_f32 %0, %1, %0" : "+v"(o[dt][r]) : "v"(alpha));
+        rescale = false;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if constexpr (kQK) {
+        if (ks + 2 < 8) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) kq[(ks + 2) % 3][t] = kfrag(ks + 2, t);
+        }
+      }
+      if constexpr (kPV) {
+        if (ks + 1 < 8) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) vq[(ks + 1) & 1][j] = vfrag(ks + 1, j);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kQK) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[t] = mfma32(kq[ks % 3][t], qf[ks], acc[t]);
+      }
+      if constexpr (kPV) {
+        const int d0 = 2 * (ks & 1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) o[d0 + j] = mfma32(vq[ks & 1][j], pf[ks >> 1], o[d0 + j]);
       }
     }
   };
 
-  for (int jt = jt_lo; jt <= jt_hi; ++jt) {
-    const int buf = (jt - jt_lo) & 1;
-    const bool has_next = jt < jt_hi;
-    if (jt == jt_hi && n_tail < kBK) {          // wave-uniform, once per work-group
-      clean_tail(buf);
-      __syncthreads();
-    }
-    if (has_next) stage_load(jt + 1, st);
-
-    // LDS fragment reads run ahead of the MFMAs that consume them (K two
-    // steps ahead, the first V slab before the softmax, later V slabs one
-    // slab ahead) so that LDS latency overlaps matrix work.
-    auto kfrag = [&](int ks, int t) {
-      const int kr = 32 * t + kp;
-      return Frag8<T>::load(&sm.k[buf][kr * kKStride + 8 * (2 * ks + lg)]);
-    };
-    auto vfrag = [&](int slab, int dt) {
-      const int dr = 32 * dt + lq;
-      return Frag8<T>::load(&sm.vt[buf][dr * kVStride + 8 * (2 * slab + lg)]);
-    };
-    Frag8<T> kq[3][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) kq[j][t] = kfrag(j, t);
-
-    // S^T accumulators start as the sheared bias band.
-    f32x16 acc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int v0 = (kBQ - 1) - a_row + 32 * t + 16 * hh + 8 * lg;
-        const float* bp = &sm.band[buf][band_shift][v0 - band_shift];
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(bp);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(bp + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[t][8 * hh + e] = x0[e];
-          acc[t][8 * hh + 4 + e] = x1[e];
-        }
-      }
-
-    // (sched_barrier keeps the compiler from sinking the reads back next to
-    // their uses, which would expose the full LDS latency on every MFMA.)
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (ks + 2 < 8) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) kq[(ks + 2) % 3][t] = kfrag(ks + 2, t);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) acc[t] = mfma32(kq[ks % 3][t], qf[ks], acc[t]);
-    }
-    Frag8<T> vq[2][4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) vq[0][dt] = vfrag(0, dt);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- online softmax (base 2), lazy rescale
+  // Softmax phase of a tile: online softmax in base 2 with a lazy rescale.
+  auto softmax_phase = [&]() {
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -300,17 +498,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
     mx = pair_max(mx);
     const float m_tile = mx * c;
     const bool need = m_tile > m_used + kRescaleSlack;
-    if (__any(need)) {
+    rescale = __any(need);
+    if (rescale) {
       // Lanes that do not need it keep their max (alpha = 1); this also keeps
       // rows that have seen no key yet (m_used = -inf) free of -inf - -inf.
-      const float alpha = need ? fast_exp2(m_used - m_tile) : 1.0f;   // -inf -> 0
+      // O itself is rescaled by the next matrix phase, before it adds this
+      // tile's P V: the matrix-phase wave has idle vector-ALU cycles, and O
+      // stays out of this phase (touching it here made the compiler copy all
+      // 64 O registers on every pass).
+      alpha = need ? fast_exp2(m_used - m_tile) : 1.0f;   // -inf -> 0
       l_sum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
       m_used = need ? m_tile : m_used;
     }
     const float msub = m_used == -INFINITY ? 0.0f : m_used;
-    Frag8<T> pf[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -321,22 +521,81 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
         pf[2 * t + hh] = Frag8<T>::pack(p);
         l_sum = pf[2 * t + hh].sum_into(l_sum);     // sums the values fed to P V
       }
+  };
 
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int slab = 0; slab < 4; ++slab) {
-      if (slab + 1 < 4) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) vq[(slab + 1) & 1][dt] = vfrag(slab + 1, dt);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vq[slab & 1][dt], pf[slab], o[dt]);
-    }
-
-    if (has_next) stage_store(buf ^ 1, st);
-    __syncthreads();
+  // V buffer 1 is read (times P^T = 0) by the first matrix phase before any
+  // V tile is loaded: zero it so that 0 * garbage cannot produce NaN.
+  {
+    u32x4* vz = reinterpret_cast<u32x4*>(&sm.vt[1][0]);
+    constexpr int kVBufSlots = kHeadDim * kVStride * (int)sizeof(T) / 16;
+    for (int i = tid; i < kVBufSlots; i += kThreads) vz[i] = u32x4{0, 0, 0, 0};
   }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pf[j] = Frag8<T>::zero();
+
+  // Prologue: stage 0 (its page from the block table directly), the slices
+  // and page numbers of stages 0 and 1; then stage 1's tiles and the slice
+  // and page numbers of stage 2.
+  if (half == 1) {
+    const int k0 = __builtin_amdgcn_readfirstlane(btab[jt_lo * kBK / kPage]);
+    keep_live(k0);
+    dma_ahead(0);
+    dma_ahead(1);
+    dma_tiles(0, k0, 0);
+  }
+  wait_all_loads();
+  __syncthreads();                                 // slices 0-1, pages of stage 1
+  if (half == 1) fix_tail(0); else band_store(0);
+  __syncthreads();                                 // stage 0 published
+  if (half == 1) {
+    int kp1, vp1;
+    stage_pages(1, kp1, vp1);
+    dma_ahead(2);
+    dma_tiles(1, kp1, vp1);
+  }
+
+  // ---- phase loop.  Waves 4-7 run one phase behind waves 0-3, and a barrier
+  // closes every phase, so the two waves sharing a SIMD are always in
+  // opposite phases: one issues MFMAs while the other runs the softmax on the
+  // vector ALU, and the two overlap.  A wave's own sequence is
+  //   M(0) S(0) M(1) S(1) ... M(n-1) S(n-1) M(n)
+  // (M = matrix phase, S = softmax phase, M(n) = PV of the last tile only);
+  // waves 0-3 run step p in phase p, waves 4-7 step p-1.  K_i and band_i live
+  // in LDS buffer i%2 through phases 2i and 2i+1, V_i in buffer i%2 through
+  // phases 2i+2 and 2i+3.  The barrier closing phase 2i+1 also publishes
+  // stage i+1 and, right after it, issues stage i+2 into the buffers of
+  // tiles i and i-1, which nobody reads any more.  The loop follows a wave's
+  // own steps, so the matrix and softmax code each appear once in it, in
+  // order (O flows straight from one to the next).  Waves 0-3 reach that
+  // barrier from their softmax phase and write the band before it; waves
+  // 4-7 reach it from their matrix phase, wait for and fix up their own tile
+  // loads before it and issue the next ones after it, before their softmax
+  // phase.  So the waves that must start MFMAs after the barrier do no
+  // staging work at all.
+  if (half == 1) __syncthreads();                  // waves 4-7 sit out phase 0
+  for (int i = 0;; ++i) {
+    matrix_phase(i);
+    if (i == n_t) break;
+    if (half == 0) {
+      __syncthreads();                             // closes phase 2i
+      softmax_phase();
+      band_store(i + 1);
+      __syncthreads();                             // closes phase 2i+1
+    } else {
+      wait_all_loads();
+      fix_tail(i + 1);
+      __syncthreads();                             // closes phase 2i+1
+      if (i + 1 < n_t) {
+        int kp, vp;
+        stage_pages(i + 2, kp, vp);
+        dma_ahead(i + 3);
+        dma_tiles(i + 2, kp, vp);
+      }
+      softmax_phase();
+      __syncthreads();                             // closes phase 2i+2
+    }
+  }
+  if (half == 0) __syncthreads();                  // closes phase 2n (M(n) of waves 0-3)
 
   // ---- epilogue: O^T register r of tile dt is dim 32dt + 8(r/4) + 4lg + r%4
   const float lt = pair_sum(l_sum);

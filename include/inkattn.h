@@ -117,7 +117,8 @@ inkattn_status_t inkattn_sconv(int32_t dtype, int32_t num_kv_heads, int32_t head
  *   bias  [Hq][R]
  *   out   [num_tokens][Hq][128]
  *   lse   float [num_tokens][Hq] = log(sum_j exp(logit_j)), or NULL
- *   max_q_len: host upper bound of the per-sequence q_len. */
+ *   max_q_len: host upper bound of the per-sequence q_len.
+ * INKATTN_ENOTSUP if the bias table (Hq * R elements) reaches 2 GiB. */
 inkattn_status_t inkattn_relattn_prefill(const inkattn_attn_desc_t* desc, int32_t num_seqs,
                                          int32_t num_tokens, int32_t max_q_len,
                                          const void* q, const void* k_cache,

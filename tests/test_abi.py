@@ -141,9 +141,13 @@ def test_num_splits_heuristic():
     assert ink.inkattn_relattn_decode_num_splits(full, 1, 300) == 3
 
 
-def test_decode_rejects_bias_table_of_2gib():
-    # the decode kernel addresses the [Hq][R] bias table with 32-bit byte offsets
+def test_prefill_and_decode_reject_bias_table_of_2gib():
+    # the kernels address the [Hq][R] bias table with 32-bit byte offsets
     lib = ink._lib._lib
+    big = _desc(dtype=1, Hq=32, R=1 << 25)            # 32 * 2^25 * 2 B = 2 GiB
+    st = lib.inkattn_relattn_prefill(ctypes.byref(big), 1, 1, 1, FAKE, FAKE, FAKE, FAKE, 1,
+                                     FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == ink.ENOTSUP
     big = _desc(dtype=1, Hq=32, R=1 << 25)            # 32 * 2^25 * 2 B = 2 GiB
     st = lib.inkattn_relattn_decode(ctypes.byref(big), 1, 100, FAKE, FAKE, FAKE, FAKE, 1, FAKE,
                                     FAKE, FAKE, None, 0, FAKE, 1 << 30, None)
