@@ -7,6 +7,9 @@
                                  tokens (bf16/fp32 MFMA, sheared bias band);
 * ``inkattn_relattn_decode``   -- split-K paged decode plus log-sum-exp merge.
 
+``inkattn_probe_mfma_bf16`` and ``inkattn_probe_stream_read`` are diagnostics
+(measured MFMA and HBM-read ceilings), not part of the attention path.
+
 The functions mirror the C ABI in ``include/inkattn.h`` one to one and take
 torch device tensors (torch supplies memory and streams only).  The helpers in
 ``kvcache`` allocate the cache in the library's layout.
@@ -17,5 +20,7 @@ from ._lib import (  # noqa: F401
     AttnDesc, InkattnError, make_desc, status_string,
     inkattn_sconv, inkattn_relattn_prefill, inkattn_relattn_decode,
     inkattn_relattn_decode_num_splits, inkattn_relattn_decode_workspace_size,
+    inkattn_probe_mfma_bf16, inkattn_probe_stream_read,
+    PROBE_MFMA_WAVES, PROBE_MFMA_CHAINS, PROBE_READ_GROUPS,
 )
 from . import kvcache  # noqa: F401

@@ -24,7 +24,11 @@ EXPORTED = (
     "inkattn_relattn_decode_workspace_size",
     "inkattn_relattn_decode",
     "inkattn_status_string",
+    "inkattn_probe_mfma_bf16",
+    "inkattn_probe_stream_read",
 )
+
+PROBE_MFMA_WAVES, PROBE_MFMA_CHAINS, PROBE_READ_GROUPS = 8, 8, 256
 
 
 class InkattnError(RuntimeError):
@@ -48,7 +52,7 @@ def make_desc(dtype, num_q_heads, num_kv_heads, window, bias_len, head_dim=128,
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m attention_sconv_amd.build`")
+            f"{LIB_PATH} is missing: build it with `python attention_sconv_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     i32, vp, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
     dp = ctypes.POINTER(AttnDesc)
@@ -67,6 +71,10 @@ def _load():
     lib.inkattn_relattn_decode.restype = i32
     lib.inkattn_status_string.argtypes = [i32]
     lib.inkattn_status_string.restype = ctypes.c_char_p
+    lib.inkattn_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
+    lib.inkattn_probe_mfma_bf16.restype = i32
+    lib.inkattn_probe_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.inkattn_probe_stream_read.restype = i32
     return lib
 
 
@@ -143,3 +151,17 @@ def inkattn_relattn_decode(desc, num_seqs, max_seq_len, q, k_cache, v_cache, blo
                                      _ptr(lse), num_splits, _ptr(workspace), workspace_bytes,
                                      _stream(stream))
     _check(st, "inkattn_relattn_decode")
+
+
+def inkattn_probe_mfma_bf16(num_groups, iters, out, stream=None):
+    """Dense bf16 MFMA loop; ``out`` is a float32 device tensor of 3*num_groups."""
+    st = _lib.inkattn_probe_mfma_bf16(num_groups, iters, _ptr(out), _stream(stream))
+    _check(st, "inkattn_probe_mfma_bf16")
+
+
+def inkattn_probe_stream_read(buf, out, stream=None):
+    """Streaming read of the whole device tensor ``buf``; ``out`` is a float32
+    device tensor of PROBE_READ_GROUPS elements."""
+    st = _lib.inkattn_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                        _stream(stream))
+    _check(st, "inkattn_probe_stream_read")

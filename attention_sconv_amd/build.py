@@ -1,6 +1,7 @@
 """Build libinkattn.so in-tree with hipcc for gfx950.
 
-Usage: python -m attention_sconv_amd.build   (or __graft_entry__.build()).
+Usage: python attention_sconv_amd/build.py   (or __graft_entry__.build()); it
+runs without importing the package, which needs the built library.
 Each .hip translation unit is compiled to an object under _build/, then all
 objects are linked into attention_sconv_amd/libinkattn.so.  Always rebuilds.
 """
@@ -15,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libinkattn.so")
-SOURCES = ["api.hip", "sconv.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "sconv.hip", "decode.hip", "prefill.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

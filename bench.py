@@ -12,8 +12,14 @@ L=16384, window 4096) and reported under "decode".
 Prints ONE JSON line.  value = algorithmic attention FLOP per step / step
 time; roofline = the prefill kernel alone (HIP events on the launch stream).
 cpu_baseline = the fp64 oracle on a bounded sample of the same workload.
+ceilings = a dense bf16 MFMA loop (with the shader clock it ran at) and a
+4 GiB streaming read, measured in the same job; frac_of_measured divides by
+them.  Before the warmup steps of each leg, about --steady-s seconds of
+untimed steps bring the shader clock to its sustained level.  Decode is also
+timed with a 1 GiB streaming read before every step (L2 and MALL evicted).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--steady-s S]
+                       [--no-cpu-baseline]
 """
 
 import argparse
@@ -121,11 +127,31 @@ def recorded_traffic(profile, sources):
     return int(fields["traffic_bytes_per_launch"].strip())
 
 
-def time_region(torch, fn_step, fn_kernel, steps, warmup):
+def steady_clocks(torch, fn_step, seconds):
+    """Run the step back to back for about ``seconds`` before any warmup or
+    timed step: the GPU raises its shader clock only under sustained load,
+    and a few milliseconds of work straight after setup would otherwise be
+    timed at a lower clock than a serving loop runs at.  Returns the number
+    of steps run (none of them is timed)."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn_step(None)
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
+def time_region(torch, fn_step, fn_kernel, steps, warmup, between=None):
     """Run warmup untimed steps, then `steps` timed steps.  Returns
-    (ms per step, mean ms of the kernel of interest), the latter from event
-    pairs recorded around that kernel on the launch stream."""
+    (ms per step, list of per-step ms of the kernel of interest), the latter
+    from event pairs recorded around that kernel on the launch stream.  With
+    ``between``, it runs before every step (outside the kernel's events; its
+    time is part of ms per step)."""
     for _ in range(warmup):
+        if between is not None:
+            between()
         fn_step(None)
     torch.cuda.synchronize()
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -135,12 +161,48 @@ def time_region(torch, fn_step, fn_kernel, steps, warmup):
     torch.cuda.synchronize()
     t0.record()
     for i in range(steps):
+        if between is not None:
+            between()
         fn_step(pairs[i])
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
-    ms_kernel = sum(a.elapsed_time(b) for a, b in pairs) / steps
-    return ms_step, ms_kernel
+    return ms_step, [a.elapsed_time(b) for a, b in pairs]
+
+
+def ceilings(torch, ink):
+    """Measured ceilings in this job: a dense bf16 MFMA loop (with the shader
+    clock it ran at) and a streaming read of 4 GiB of device memory."""
+    groups, iters = 1024, 12000
+    out = torch.zeros(3 * groups, dtype=torch.float32, device="cuda")
+    ink.inkattn_probe_mfma_bf16(groups, iters, out)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    ink.inkattn_probe_mfma_bf16(groups, iters, out)
+    e[1].record()
+    torch.cuda.synchronize()
+    flop = groups * iters * ink.PROBE_MFMA_WAVES * ink.PROBE_MFMA_CHAINS * 32768
+    mfma = flop / (e[0].elapsed_time(e[1]) * 1e-3) / 1e12
+    r = out.view(groups, 3).cpu().numpy()
+    sclk = float(np.median(r[:, 1] / r[:, 2] * 100.0))
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(7)
+    sink = torch.zeros(ink.PROBE_READ_GROUPS, dtype=torch.float32, device="cuda")
+    ink.inkattn_probe_stream_read(buf, sink)
+    reps = 5
+    e[0].record()
+    for _ in range(reps):
+        ink.inkattn_probe_stream_read(buf, sink)
+    e[1].record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (e[0].elapsed_time(e[1]) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(mfma, 1), "sclk_mhz_under_mfma": round(sclk),
+            "hbm_read_gbs": round(gbs, 1),
+            "note": "inkattn_probe_mfma_bf16 (1024 groups x 8 waves x 8 chains of "
+                    "32x32x16 bf16) and inkattn_probe_stream_read (4 GiB, 256 groups x "
+                    "256 threads x 8 loads of 16 B in flight), same job"}
 
 
 def cpu_baseline(case, budget_s=10.0):
@@ -187,6 +249,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--steady-s", type=float, default=0.3,
+                    help="seconds of untimed back-to-back steps before the warmup steps, "
+                         "so that the timed steps run at the sustained shader clock")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the bench, run one plain device-to-device copy of this "
                          "many bytes (reference kernel for HBM traffic counters)")
@@ -216,7 +281,9 @@ def main():
 
     print(f"[bench] prefill {wl.name}: warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
-    ms_step, ms_prefill = time_region(torch, step, None, args.steps, args.warmup)
+    n_steady = steady_clocks(torch, step, args.steady_s)
+    ms_step, ks = time_region(torch, step, None, args.steps, args.warmup)
+    ms_prefill = sum(ks) / len(ks)
     value = flop / (ms_step * 1e-3) / 1e12
     achieved = flop / (ms_prefill * 1e-3) / 1e12
 
@@ -244,7 +311,10 @@ def main():
                          ["attention_sconv_amd/csrc/prefill.hip",
                           "attention_sconv_amd/csrc/device_common.h"]),
                      "kernel": "prefill_kernel<bf16>", "ms": round(ms_prefill, 4),
+                     "ms_median": round(float(np.median(ks)), 4),
+                     "ms_min": round(min(ks), 4),
                      "algorithmic_flop": flop},
+        "steady_clock_steps": n_steady,
     }
 
     # ---------------- decode: sconv (1 token/seq) + split-K decode, 16K SWA
@@ -266,21 +336,48 @@ def main():
                 ev[1].record()
 
         print(f"[bench] decode {dwl.name}", file=sys.stderr, flush=True)
-        d_ms_step, d_ms = time_region(torch, dstep, None, max(args.steps, 20), args.warmup)
+        d_steps = max(args.steps, 20)
+        steady_clocks(torch, dstep, args.steady_s)
+        d_ms_step, dks = time_region(torch, dstep, None, d_steps, args.warmup)
+        d_ms = sum(dks) / len(dks)
         gbs = kv_bytes / (d_ms * 1e-3) / 1e9
+        # The same with a streaming read of 1 GiB before every step, which
+        # evicts the attended K/V from L2 and the 256 MB MALL (with clean
+        # lines, so no write-back competes with the decode): decode then
+        # reads HBM.
+        import attention_sconv_amd as ink
+        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        sink = torch.zeros(ink.PROBE_READ_GROUPS, dtype=torch.float32, device="cuda")
+        _, fks = time_region(torch, dstep, None, d_steps, args.warmup,
+                             between=lambda: ink.inkattn_probe_stream_read(flush, sink))
+        del flush
+        f_ms = float(np.median(fks))
+        f_gbs = kv_bytes / (f_ms * 1e-3) / 1e9
         result["decode"] = {
             "workload": dwl.name + ": " + dwl.description,
             "ms_per_step": round(d_ms_step, 4), "ms_decode": round(d_ms, 4),
             "num_splits": dd.num_splits,
             "kv_bytes": kv_bytes, "achieved": round(gbs, 1), "unit": "GB/s",
             "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "ms_decode_median": round(float(np.median(dks)), 4), "ms_decode_min": round(min(dks), 4),
+            "flushed": {"ms_median": round(f_ms, 4), "ms_min": round(min(fks), 4),
+                        "achieved": round(f_gbs, 1), "frac": round(f_gbs / PEAK_HBM_GBS, 4),
+                        "note": "1 GiB streaming read before every step (L2 and MALL evicted)"},
             "traffic": recorded_traffic(
                 "decode_split_bf16_swa_decode_16k.traffic.txt",
                 ["attention_sconv_amd/csrc/decode.hip",
                  "attention_sconv_amd/csrc/device_common.h"]),
-            "note": "L2/MALL not flushed between steps",
+            "note": "achieved/frac: back-to-back steps; flushed: L2/MALL evicted before each step",
         }
         del dd
+
+    import attention_sconv_amd as ink
+    print("[bench] measured ceilings", file=sys.stderr, flush=True)
+    ceil = ceilings(torch, ink)
+    result["ceilings"] = ceil
+    result["roofline"]["frac_of_measured"] = round(achieved / ceil["mfma_bf16_tflops"], 4)
+    if "decode" in result:
+        result["decode"]["frac_of_measured"] = round(gbs / ceil["hbm_read_gbs"], 4)
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

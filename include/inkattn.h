@@ -170,6 +170,38 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
 /* Static, NUL-terminated description of a status code. */
 const char* inkattn_status_string(int32_t status);
 
+/* ---- Diagnostics: measured ceilings for the roofline denominators --------
+ * Not part of the attention path.  A benchmark runs them in the same job as
+ * the kernels to report each kernel's fraction of what this GPU sustains
+ * beside its fraction of the published peaks.  Both are asynchronous on
+ * `stream` (a hipStream_t, NULL = default stream). */
+
+#define INKATTN_PROBE_MFMA_WAVES 8
+#define INKATTN_PROBE_MFMA_CHAINS 8
+#define INKATTN_PROBE_READ_GROUPS 256
+
+/* Dense bf16 MFMA loop: num_groups work-groups of INKATTN_PROBE_MFMA_WAVES
+ * waves (two per SIMD), each wave running iters rounds of
+ * INKATTN_PROBE_MFMA_CHAINS independent v_mfma_f32_32x32x16_bf16 chains on
+ * operands with random mantissas.  Work = num_groups * iters * WAVES * CHAINS
+ * * 32768 flop.
+ * out: device float[3 * num_groups]; group g writes an accumulator sum (a
+ * sink), then the shader-clock cycles and the 100 MHz real-time ticks of its
+ * first wave's loop (cycles / ticks * 100 = sclk in MHz).
+ * INKATTN_EINVAL if num_groups < 1, iters < 1 or out is NULL. */
+inkattn_status_t inkattn_probe_mfma_bf16(int32_t num_groups, int32_t iters, float* out,
+                                         void* stream);
+
+/* Streaming read of `bytes` bytes of device memory at `buf` (16-byte words,
+ * grid-stride, INKATTN_PROBE_READ_GROUPS work-groups of 256 threads, eight
+ * 16-byte loads in flight per thread).  The memory is only read.
+ * out: device float[INKATTN_PROBE_READ_GROUPS], a sink that is written only
+ * if the XOR of the data read equals one fixed constant.
+ * INKATTN_EINVAL if buf or out is NULL, bytes is 0, or buf / bytes are not
+ * multiples of 16. */
+inkattn_status_t inkattn_probe_stream_read(const void* buf, size_t bytes, float* out,
+                                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -156,3 +156,19 @@ def test_prefill_and_decode_reject_bias_table_of_2gib():
     st = lib.inkattn_relattn_decode(ctypes.byref(big32), 1, 100, FAKE, FAKE, FAKE, FAKE, 1,
                                     FAKE, FAKE, FAKE, None, 0, FAKE, 1 << 30, None)
     assert st == ink.ENOTSUP
+
+
+def test_probes_reject_bad_arguments():
+    lib = ctypes.CDLL(ink.LIB_PATH)
+    lib.inkattn_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+    lib.inkattn_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+    assert lib.inkattn_probe_mfma_bf16(0, 10, FAKE, None) == ink.EINVAL
+    assert lib.inkattn_probe_mfma_bf16(4, 0, FAKE, None) == ink.EINVAL
+    assert lib.inkattn_probe_mfma_bf16(4, 10, None, None) == ink.EINVAL
+    assert lib.inkattn_probe_stream_read(None, 1024, FAKE, None) == ink.EINVAL
+    assert lib.inkattn_probe_stream_read(FAKE, 0, FAKE, None) == ink.EINVAL
+    assert lib.inkattn_probe_stream_read(FAKE + 4, 1024, FAKE, None) == ink.EINVAL
+    assert lib.inkattn_probe_stream_read(FAKE, 1000, FAKE, None) == ink.EINVAL
+    assert lib.inkattn_probe_stream_read(FAKE, 1024, None, None) == ink.EINVAL
