@@ -203,18 +203,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   const int32_t* btab = A.block_table + (size_t)b * A.max_blocks;
 
   // Q^T fragments (B operand): d = 16*ks + 8*lg + e.
+  // Loaded in the prologue, together with the first stage.
   Frag8<T> qf[8];
-  {
-    const T* qrow = qp + ((size_t)(tok0 + row0 + a_row) * A.Hq + h) * kHeadDim + 8 * lg;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = row_ok ? Frag8<T>::load(qrow + 16 * ks) : Frag8<T>::zero();
-    // Consume the fragments here, so that the compiler's own memory-wait
-    // bookkeeping sees these loads finished before the phase loop and never
-    // waits there (such a wait would also stall on the in-flight tile loads,
-    // which the bookkeeping cannot see).
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) keep_live(qf[ks]);
-  }
 
   const float sqrt_d = 11.313708498984761f;               // sqrt(128)
   const float c = kLog2e / sqrt_d;
@@ -371,8 +361,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   // Bias band of stage x from its raw slice (published by an earlier
   // barrier): pre-multiplied by sqrt(128), -inf outside the causal window,
   // distances >= R take bias[R-1].  Four copies shifted by one entry.
-  const float bias_last = to_f32(bias_h[A.R - 1]);
-  keep_live(bias_last);
+  float bias_last;                                  // loaded in the prologue
   // Written by waves 0-3 (256 threads), at the end of their softmax phase.
   auto band_store = [&](int x) {
     if (x >= n_t) return;
@@ -536,14 +525,30 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   // Prologue: stage 0 (its page from the block table directly), the slices
   // and page numbers of stages 0 and 1; then stage 1's tiles and the slice
   // and page numbers of stage 2.
-  if (half == 1) {
-    const int k0 = __builtin_amdgcn_readfirstlane(btab[jt_lo * kBK / kPage]);
-    keep_live(k0);
-    dma_ahead(0);
-    dma_ahead(1);
-    dma_tiles(0, k0, 0);
+  // The plain loads (the first page number, bias[R-1], the Q fragments) are
+  // issued first and the first stage's DMA right behind them, so their
+  // latencies overlap; all of them are consumed after the wait below, so the
+  // compiler's own memory-wait bookkeeping sees them finished before the
+  // phase loop and never waits there (such a wait would also stall on the
+  // in-flight tile loads, which the bookkeeping cannot see).
+  {
+    int k0 = 0;
+    if (half == 1) k0 = __builtin_amdgcn_readfirstlane(btab[jt_lo * kBK / kPage]);
+    bias_last = to_f32(bias_h[A.R - 1]);
+    const T* qrow = qp + ((size_t)(tok0 + row0 + a_row) * A.Hq + h) * kHeadDim + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = row_ok ? Frag8<T>::load(qrow + 16 * ks) : Frag8<T>::zero();
+    if (half == 1) {
+      keep_live(k0);
+      dma_ahead(0);
+      dma_ahead(1);
+      dma_tiles(0, k0, 0);
+    }
   }
   wait_all_loads();
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) keep_live(qf[ks]);
+  keep_live(bias_last);
   __syncthreads();                                 // slices 0-1, pages of stage 1
   if (half == 1) fix_tail(0); else band_store(0);
   __syncthreads();                                 // stage 0 published
