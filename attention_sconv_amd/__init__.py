@@ -5,7 +5,9 @@
                                  three-token state update;
 * ``inkattn_relattn_prefill``  -- relative-position GQA attention over new
                                  tokens (bf16/fp32 MFMA, sheared bias band);
-* ``inkattn_relattn_decode``   -- split-K paged decode plus log-sum-exp merge.
+* ``inkattn_relattn_decode``   -- split-K paged decode plus log-sum-exp merge;
+* ``inkattn_relattn_decode_mq`` -- the same for a few query tokens per sequence
+                                 (verification of multi-token-prediction drafts).
 
 ``inkattn_probe_mfma_bf16`` and ``inkattn_probe_stream_read`` are diagnostics
 (measured MFMA and HBM-read ceilings), not part of the attention path.
@@ -20,6 +22,8 @@ from ._lib import (  # noqa: F401
     AttnDesc, InkattnError, make_desc, status_string,
     inkattn_sconv, inkattn_relattn_prefill, inkattn_relattn_decode,
     inkattn_relattn_decode_num_splits, inkattn_relattn_decode_workspace_size,
+    inkattn_relattn_decode_mq, inkattn_relattn_decode_mq_num_splits,
+    inkattn_relattn_decode_mq_workspace_size,
     inkattn_probe_mfma_bf16, inkattn_probe_stream_read,
     PROBE_MFMA_WAVES, PROBE_MFMA_CHAINS, PROBE_READ_GROUPS,
 )

@@ -23,6 +23,9 @@ EXPORTED = (
     "inkattn_relattn_decode_num_splits",
     "inkattn_relattn_decode_workspace_size",
     "inkattn_relattn_decode",
+    "inkattn_relattn_decode_mq_num_splits",
+    "inkattn_relattn_decode_mq_workspace_size",
+    "inkattn_relattn_decode_mq",
     "inkattn_status_string",
     "inkattn_probe_mfma_bf16",
     "inkattn_probe_stream_read",
@@ -69,6 +72,13 @@ def _load():
     lib.inkattn_relattn_decode.argtypes = [dp, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                            i32, vp, sz, vp]
     lib.inkattn_relattn_decode.restype = i32
+    lib.inkattn_relattn_decode_mq_num_splits.argtypes = [dp, i32, i32, i32]
+    lib.inkattn_relattn_decode_mq_num_splits.restype = i32
+    lib.inkattn_relattn_decode_mq_workspace_size.argtypes = [dp, i32, i32, i32, i32, i32]
+    lib.inkattn_relattn_decode_mq_workspace_size.restype = sz
+    lib.inkattn_relattn_decode_mq.argtypes = [dp, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp,
+                                              vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.inkattn_relattn_decode_mq.restype = i32
     lib.inkattn_status_string.argtypes = [i32]
     lib.inkattn_status_string.restype = ctypes.c_char_p
     lib.inkattn_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
@@ -165,3 +175,29 @@ def inkattn_probe_stream_read(buf, out, stream=None):
     st = _lib.inkattn_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
                                         _stream(stream))
     _check(st, "inkattn_probe_stream_read")
+
+
+def inkattn_relattn_decode_mq_num_splits(desc, num_seqs, max_q_len, max_seq_len):
+    return int(_lib.inkattn_relattn_decode_mq_num_splits(ctypes.byref(desc), num_seqs,
+                                                         max_q_len, max_seq_len))
+
+
+def inkattn_relattn_decode_mq_workspace_size(desc, num_seqs, num_tokens, max_q_len,
+                                             max_seq_len, num_splits=0):
+    return int(_lib.inkattn_relattn_decode_mq_workspace_size(
+        ctypes.byref(desc), num_seqs, num_tokens, max_q_len, max_seq_len, num_splits))
+
+
+def inkattn_relattn_decode_mq(desc, num_seqs, num_tokens, max_q_len, max_seq_len, q, k_cache,
+                              v_cache, block_table, max_blocks_per_seq, cu_seqlens_q, seq_lens,
+                              bias, out, lse, num_splits, workspace, workspace_bytes=None,
+                              stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.inkattn_relattn_decode_mq(ctypes.byref(desc), num_seqs, num_tokens, max_q_len,
+                                        max_seq_len, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(block_table), max_blocks_per_seq,
+                                        _ptr(cu_seqlens_q), _ptr(seq_lens), _ptr(bias),
+                                        _ptr(out), _ptr(lse), num_splits, _ptr(workspace),
+                                        workspace_bytes, _stream(stream))
+    _check(st, "inkattn_relattn_decode_mq")

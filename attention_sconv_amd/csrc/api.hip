@@ -13,6 +13,7 @@ namespace {
 
 constexpr int kCUs = 256;                  // MI355X compute units
 constexpr int kDecodeTargetGroups = kCUs;   // (seq, kv-head, split) work-groups, one per CU
+constexpr int kMaxDecodeQueries = 16;       // query tokens per sequence in one decode call
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -32,18 +33,24 @@ AttnShape shape_of(const inkattn_attn_desc_t* d) {
 }
 
 // Number of 128-token blocks that the attended key range of the longest
-// sequence can touch.
-int64_t blocks_in_range(const inkattn_attn_desc_t* d, int64_t max_seq_len) {
+// sequence can touch (its q_len query tokens together see window + q_len - 1
+// keys).
+int64_t blocks_in_range(const inkattn_attn_desc_t* d, int64_t max_seq_len, int64_t max_q_len) {
   const int64_t all = (max_seq_len + 127) / 128;
   if (d->window == 0) return all;
-  const int64_t keys = d->window < max_seq_len ? d->window : max_seq_len;
+  const int64_t want = (int64_t)d->window + max_q_len - 1;
+  const int64_t keys = want < max_seq_len ? want : max_seq_len;
   const int64_t span = (keys + 127) / 128 + 1;   // +1: range need not be block aligned
   return span < all ? span : all;
 }
 
-int32_t auto_splits(const inkattn_attn_desc_t* d, int32_t num_seqs, int32_t max_seq_len) {
-  const int64_t pairs = (int64_t)num_seqs * d->num_kv_heads;
-  const int64_t nblk = blocks_in_range(d, max_seq_len);
+// Splits so that the (sequence, kv-head, column tile, split) work-groups
+// about fill the GPU once, never more splits than blocks in the range.
+int32_t auto_splits(const inkattn_attn_desc_t* d, int32_t num_seqs, int32_t max_seq_len,
+                    int32_t max_q_len = 1) {
+  const int64_t pairs = (int64_t)num_seqs * d->num_kv_heads *
+                        inkattn::decode_column_tiles(d->num_q_heads / d->num_kv_heads, max_q_len);
+  const int64_t nblk = blocks_in_range(d, max_seq_len, max_q_len);
   if (pairs <= 0 || nblk <= 0) return 1;
   int64_t s = (kDecodeTargetGroups + pairs - 1) / pairs;
   if (s > nblk) s = nblk;
@@ -151,6 +158,7 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
   if (num_seqs < 0 || max_seq_len < 0 || num_splits < 0) return INKATTN_EINVAL;
   if (num_seqs == 0) return INKATTN_OK;
   if (max_seq_len < 1 || max_blocks_per_seq < 1) return INKATTN_EINVAL;
+  if (num_seqs > 65535) return INKATTN_ENOTSUP;                  // one grid row per sequence
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !bias || !out || !workspace)
     return INKATTN_EINVAL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
@@ -163,9 +171,72 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
   const size_t rows = (size_t)num_seqs * desc->num_q_heads * (size_t)s;
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = part_o + rows * 128;
-  return from_hip(inkattn::launch_decode(shape_of(desc), num_seqs, s, q, k_cache, v_cache,
-                                         block_table, max_blocks_per_seq, seq_lens, bias,
-                                         out, lse, part_o, part_lse, (hipStream_t)stream));
+  return from_hip(inkattn::launch_decode(shape_of(desc), num_seqs, num_seqs, 1, s, q, k_cache,
+                                         v_cache, block_table, max_blocks_per_seq, nullptr,
+                                         seq_lens, bias, out, lse, part_o, part_lse,
+                                         (hipStream_t)stream));
+}
+
+int32_t inkattn_relattn_decode_mq_num_splits(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                             int32_t max_q_len, int32_t max_seq_len) {
+  if (check_desc(desc) != INKATTN_OK || num_seqs < 1 || max_seq_len < 1 || max_q_len < 1 ||
+      max_q_len > kMaxDecodeQueries)
+    return 1;
+  return auto_splits(desc, num_seqs, max_seq_len, max_q_len);
+}
+
+size_t inkattn_relattn_decode_mq_workspace_size(const inkattn_attn_desc_t* desc,
+                                                int32_t num_seqs, int32_t num_tokens,
+                                                int32_t max_q_len, int32_t max_seq_len,
+                                                int32_t num_splits) {
+  if (check_desc(desc) != INKATTN_OK || num_seqs < 0 || num_tokens < 0 || max_seq_len < 0 ||
+      num_splits < 0 || max_q_len < 1 || max_q_len > kMaxDecodeQueries)
+    return 0;
+  const int64_t s =
+      num_splits == 0 ? auto_splits(desc, num_seqs, max_seq_len, max_q_len) : num_splits;
+  const size_t rows = (size_t)num_tokens * desc->num_q_heads * (size_t)s;
+  return rows * 128 * sizeof(float) + ((rows * sizeof(float) + 15) & ~(size_t)15);
+}
+
+inkattn_status_t inkattn_relattn_decode_mq(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                           int32_t num_tokens, int32_t max_q_len,
+                                           int32_t max_seq_len, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const int32_t* block_table,
+                                           int32_t max_blocks_per_seq,
+                                           const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                           const void* bias, void* out, float* lse,
+                                           int32_t num_splits, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  inkattn_status_t st = check_desc(desc);
+  if (st != INKATTN_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || max_seq_len < 0 || num_splits < 0 || max_q_len < 0)
+    return INKATTN_EINVAL;
+  if (num_seqs == 0 || num_tokens == 0) return INKATTN_OK;
+  if (max_q_len < 1 || num_tokens < num_seqs || max_seq_len < 1 || max_blocks_per_seq < 1)
+    return INKATTN_EINVAL;
+  if (max_q_len > kMaxDecodeQueries) return INKATTN_ENOTSUP;
+  const int n_ct = inkattn::decode_column_tiles(desc->num_q_heads / desc->num_kv_heads, max_q_len);
+  if ((int64_t)num_seqs * n_ct > 65535) return INKATTN_ENOTSUP;
+  if (!q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !seq_lens || !bias ||
+      !out || !workspace)
+    return INKATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(workspace))
+    return INKATTN_EINVAL;
+  if (bias_table_too_large(desc)) return INKATTN_ENOTSUP;
+  const int32_t s =
+      num_splits == 0 ? auto_splits(desc, num_seqs, max_seq_len, max_q_len) : num_splits;
+  const size_t need = inkattn_relattn_decode_mq_workspace_size(desc, num_seqs, num_tokens,
+                                                               max_q_len, max_seq_len, s);
+  if (workspace_bytes < need) return INKATTN_EINVAL;
+  const size_t rows = (size_t)num_tokens * desc->num_q_heads * (size_t)s;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = part_o + rows * 128;
+  return from_hip(inkattn::launch_decode(shape_of(desc), num_seqs, num_tokens, max_q_len, s, q,
+                                         k_cache, v_cache, block_table, max_blocks_per_seq,
+                                         cu_seqlens_q, seq_lens, bias, out, lse, part_o,
+                                         part_lse, (hipStream_t)stream));
 }
 
 }  // extern "C"

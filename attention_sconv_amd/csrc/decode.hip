@@ -46,26 +46,37 @@ constexpr int kDecodeThreads = 64 * kDecodeWaves;
 
 template <typename T>
 __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
-    int Hq, int Hkv, int window, int R, int S, const T* __restrict__ q,
+    int Hq, int Hkv, int window, int R, int S, int n_ct, const T* __restrict__ q,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
-    const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seq_lens,
-    const T* __restrict__ bias, float* __restrict__ part_o, float* __restrict__ part_lse,
-    T* __restrict__ out, float* __restrict__ lse) {
+    const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ seq_lens, const T* __restrict__ bias,
+    float* __restrict__ part_o, float* __restrict__ part_lse, T* __restrict__ out,
+    float* __restrict__ lse) {
   __shared__ float sm_m[kDecodeWaves][16];
   __shared__ float sm_l[kDecodeWaves][16];
   __shared__ float sm_o[kDecodeWaves][16][kHeadDim + 4];
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  const int b = blockIdx.z / n_ct;
+  const int ct = blockIdx.z % n_ct;  // column tile: columns 16ct .. 16ct+15
   const int G = Hq / Hkv;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  const int col = lane & 15;      // MFMA column (query head in group) / row index for A loads
+  const int col = lane & 15;      // MFMA column / row index for A loads
   const int grp = lane >> 4;      // lane group 0..3
 
+  // The query tokens of sequence b (one for plain decode; up to a few draft
+  // tokens when several positions are verified at once) sit at positions
+  // L-q_len .. L-1.  Column c of the work-group's tiles is (token c / G,
+  // head c % G of the group); this work-group computes columns 16ct .. +15.
+  const int tok0 = cu_q != nullptr ? cu_q[b] : b;
+  const int q_len = cu_q != nullptr ? cu_q[b + 1] - tok0 : 1;
+  const int n_cols = G * q_len;
+  if (16 * ct >= n_cols) return;                 // (wave-uniform: the whole work-group)
   const int L = seq_lens[b];
-  const int kstart = window > 0 ? max(0, L - window) : 0;
+  const int pos0 = L - q_len;                    // position of the first query token
+  const int kstart = window > 0 ? max(0, pos0 - window + 1) : 0;
   const int blk_first = kstart >> 7;
   const int blk_last = (L - 1) >> 7;
   const int nblk = blk_last - blk_first + 1;
@@ -74,17 +85,22 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
   const int my_hi = min(my_lo + bps, blk_last + 1);
   const int n_items = 4 * max(my_hi - my_lo, 0);   // item i: page my_lo + i/4, keys 32(i%4) ..
 
-  const bool head_ok = col < G;
-  const int h = kvh * G + col;
+  const int gc = 16 * ct + col;
+  const bool head_ok = gc < n_cols;             // this lane's column is a real (token, head)
+  const int token = head_ok ? gc / G : 0;
+  const int h = kvh * G + (head_ok ? gc % G : 0);
+  const int pos = pos0 + token;                  // this column's query position
+  const int k_lo = window > 0 ? max(0, pos - window + 1) : 0;    // its visible keys: k_lo .. pos
   Frag8<T> qf[4];
 #pragma unroll
   for (int ds = 0; ds < 4; ++ds)
-    qf[ds] = head_ok ? Frag8<T>::load(q + ((size_t)b * Hq + h) * kHeadDim + 32 * ds + 8 * grp)
+    qf[ds] = head_ok ? Frag8<T>::load(q + ((size_t)(tok0 + token) * Hq + h) * kHeadDim + 32 * ds +
+                                      8 * grp)
                      : Frag8<T>::zero();
   // Bias row of this lane's head, as an element index into the whole table
   // (the entry point keeps the table under 2 GiB).
   const rsrc_t bias_r = make_rsrc(bias, (uint32_t)((size_t)Hq * R * sizeof(T)));
-  const uint32_t bias_row = (uint32_t)(head_ok ? h : 0) * (uint32_t)R;
+  const uint32_t bias_row = (uint32_t)h * (uint32_t)R;
 
   const float c = 0.08838834764831845f * kLog2e;   // log2(e) / sqrt(128)
   float m = -INFINITY;                             // running max (log2 units)
@@ -116,7 +132,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
     const int j0 = blk * kPage + 32 * u + 8 * grp;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      bb[e] = buf_load_elem<T>(bias_r, (bias_row + min(max(L - 1 - (j0 + e), 0), R - 1)) * sizeof(T));
+      bb[e] = buf_load_elem<T>(bias_r, (bias_row + min(max(pos - (j0 + e), 0), R - 1)) * sizeof(T));
     const size_t base = page_base(blk);
     const rsrc_t kr = make_rsrc(k_cache + base, kPageBytes);
     const rsrc_t vr = make_rsrc(v_cache + base, kPageBytes);
@@ -148,7 +164,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = j0 + e;
-      const bool ok = head_ok && j >= kstart && j < L;
+      const bool ok = head_ok && j >= k_lo && j <= pos;
       x[e] = ok ? sacc[e >> 2][e & 3] * c + to_f32(bb[e]) * kLog2e : -INFINITY;
       mx = fmaxf(mx, x[e]);
     }
@@ -227,13 +243,16 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
     for (int r = 0; r < 4; ++r) sm_o[wave][col][16 * dt + 4 * grp + r] = o[dt][r];
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kDecodeThreads) {
-    const int hh = idx / kHeadDim;
+  const int tile_cols = min(16, n_cols - 16 * ct);
+  for (int idx = threadIdx.x; idx < tile_cols * kHeadDim; idx += kDecodeThreads) {
+    const int hh = idx / kHeadDim;               // column within the tile
     const int d = idx % kHeadDim;
+    const int cg = 16 * ct + hh;
+    const size_t orow = (size_t)(tok0 + cg / G) * Hq + kvh * G + cg % G;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm_m[w][hh]);
-    const size_t row = ((size_t)b * Hq + kvh * G + hh) * S + split;
+    const size_t row = orow * S + split;
     if (M == -INFINITY) {
       part_o[row * kHeadDim + d] = 0.0f;
       if (d == 0) part_lse[row] = -INFINITY;
@@ -249,7 +268,6 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
     if (S == 1) {
       // A single split is the whole key range: write the result directly
       // (no merge pass).
-      const size_t orow = (size_t)b * Hq + kvh * G + hh;
       out[orow * kHeadDim + d] = from_f32<T>(num / den);
       if (lse != nullptr && d == 0) lse[orow] = (M + fast_log2(den)) * kLn2;
     } else {
@@ -264,9 +282,9 @@ __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(
     int Hq, int S, const float* __restrict__ part_o, const float* __restrict__ part_lse,
     T* __restrict__ out, float* __restrict__ lse) {
   const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  const int t = blockIdx.y;                      // query token
   const int d = threadIdx.x;
-  const size_t row0 = ((size_t)b * Hq + h) * S;
+  const size_t row0 = ((size_t)t * Hq + h) * S;
   float M = -INFINITY;
   for (int s = 0; s < S; ++s) M = fmaxf(M, part_lse[row0 + s]);
   float num = 0.0f, den = 0.0f;
@@ -277,34 +295,36 @@ __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(
     num += w * part_o[(row0 + s) * kHeadDim + d];
     den += w;
   }
-  out[((size_t)b * Hq + h) * kHeadDim + d] = from_f32<T>(num / den);
-  if (lse != nullptr && d == 0) lse[(size_t)b * Hq + h] = M + fast_log2(den) * kLn2;
+  out[((size_t)t * Hq + h) * kHeadDim + d] = from_f32<T>(num / den);
+  if (lse != nullptr && d == 0) lse[(size_t)t * Hq + h] = M + fast_log2(den) * kLn2;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_splits, const void* q,
-                         const void* k_cache, const void* v_cache,
-                         const int32_t* block_table, int max_blocks_per_seq,
+hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_tokens, int max_q_len,
+                         int num_splits, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table,
+                         int max_blocks_per_seq, const int32_t* cu_seqlens_q,
                          const int32_t* seq_lens, const void* bias, void* out, float* lse,
                          float* part_o, float* part_lse, hipStream_t stream) {
-  dim3 grid(num_splits, s.Hkv, num_seqs);
-  dim3 mgrid(s.Hq, num_seqs);
+  const int n_ct = decode_column_tiles(s.Hq / s.Hkv, max_q_len);
+  dim3 grid(num_splits, s.Hkv, num_seqs * n_ct);
+  dim3 mgrid(s.Hq, num_tokens);
   if (s.dtype == kDtypeBf16) {
     hipLaunchKernelGGL(decode_split_kernel<bf16>, grid, dim3(kDecodeThreads), 0, stream, s.Hq,
-                       s.Hkv, s.window, s.bias_len, num_splits, (const bf16*)q,
+                       s.Hkv, s.window, s.bias_len, num_splits, n_ct, (const bf16*)q,
                        (const bf16*)k_cache, (const bf16*)v_cache, block_table,
-                       max_blocks_per_seq, seq_lens, (const bf16*)bias, part_o, part_lse,
-                       (bf16*)out, lse);
+                       max_blocks_per_seq, cu_seqlens_q, seq_lens, (const bf16*)bias, part_o,
+                       part_lse, (bf16*)out, lse);
     if (num_splits > 1)
       hipLaunchKernelGGL(decode_merge_kernel<bf16>, mgrid, dim3(kHeadDim), 0, stream, s.Hq,
                          num_splits, part_o, part_lse, (bf16*)out, lse);
   } else {
     hipLaunchKernelGGL(decode_split_kernel<float>, grid, dim3(kDecodeThreads), 0, stream, s.Hq,
-                       s.Hkv, s.window, s.bias_len, num_splits, (const float*)q,
+                       s.Hkv, s.window, s.bias_len, num_splits, n_ct, (const float*)q,
                        (const float*)k_cache, (const float*)v_cache, block_table,
-                       max_blocks_per_seq, seq_lens, (const float*)bias, part_o, part_lse,
-                       (float*)out, lse);
+                       max_blocks_per_seq, cu_seqlens_q, seq_lens, (const float*)bias, part_o,
+                       part_lse, (float*)out, lse);
     if (num_splits > 1)
       hipLaunchKernelGGL(decode_merge_kernel<float>, mgrid, dim3(kHeadDim), 0, stream, s.Hq,
                          num_splits, part_o, part_lse, (float*)out, lse);

@@ -27,9 +27,16 @@ hipError_t launch_prefill(const AttnShape& s, int num_seqs, int max_q_len, const
                           const int32_t* cu_seqlens_q, const int32_t* seq_lens,
                           const void* bias, void* out, float* lse, hipStream_t stream);
 
-hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_splits, const void* q,
-                         const void* k_cache, const void* v_cache,
-                         const int32_t* block_table, int max_blocks_per_seq,
+// Decode over num_seqs sequences with 1 .. max_q_len query tokens each
+// (cu_seqlens_q == nullptr: exactly one token per sequence, token b of
+// sequence b).  The (token, head) columns of a kv-head group are computed in
+// tiles of 16 by separate work-groups.
+constexpr int decode_column_tiles(int G, int max_q_len) { return (G * max_q_len + 15) / 16; }
+
+hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_tokens, int max_q_len,
+                         int num_splits, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table,
+                         int max_blocks_per_seq, const int32_t* cu_seqlens_q,
                          const int32_t* seq_lens, const void* bias, void* out, float* lse,
                          float* part_o, float* part_lse, hipStream_t stream);
 

@@ -167,6 +167,43 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
                                         int32_t num_splits, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
+/* Decode of several query tokens per sequence at once: the verification
+ * step of multi-token prediction, where a sequence's last accepted token and
+ * its draft tokens are checked together ([A] Model Architecture / MTP: up to
+ * 9 tokens per forward step; [A] Performance: MTP8 with a mean acceptance
+ * length of 4.5).  Sequence b has q_len = cu_seqlens_q[b+1] -
+ * cu_seqlens_q[b] query tokens (1 <= q_len <= max_q_len <= 16) at positions
+ * seq_lens[b]-q_len .. seq_lens[b]-1, whose keys and values are already in
+ * the cache (inkattn_sconv); each attends causally (and within the window)
+ * with the logit of inkattn_relattn_prefill, so the result equals prefill
+ * of those tokens with the sequence's earlier tokens as context.  K and V
+ * are read once per (sequence, kv-head, split) for every 16 (token, q-head)
+ * pairs of the group.
+ *   q    [num_tokens][Hq][128]        out [num_tokens][Hq][128]
+ *   lse  float [num_tokens][Hq], or NULL
+ *   cu_seqlens_q int32 [num_seqs+1], cu_seqlens_q[num_seqs] = num_tokens
+ *   workspace: device, 16-byte aligned, >= inkattn_relattn_decode_mq_
+ *              workspace_size(...) bytes; caller-owned scratch.
+ *   num_splits: 0 = automatic (inkattn_relattn_decode_mq_num_splits).
+ * Errors as inkattn_relattn_decode; INKATTN_ENOTSUP for max_q_len > 16 or
+ * num_seqs * ceil(Hq/Hkv * max_q_len / 16) > 65535. */
+int32_t inkattn_relattn_decode_mq_num_splits(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                             int32_t max_q_len, int32_t max_seq_len);
+size_t inkattn_relattn_decode_mq_workspace_size(const inkattn_attn_desc_t* desc,
+                                                int32_t num_seqs, int32_t num_tokens,
+                                                int32_t max_q_len, int32_t max_seq_len,
+                                                int32_t num_splits);
+inkattn_status_t inkattn_relattn_decode_mq(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                           int32_t num_tokens, int32_t max_q_len,
+                                           int32_t max_seq_len, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const int32_t* block_table,
+                                           int32_t max_blocks_per_seq,
+                                           const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                           const void* bias, void* out, float* lse,
+                                           int32_t num_splits, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* inkattn_status_string(int32_t status);
 

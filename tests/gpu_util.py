@@ -124,6 +124,26 @@ class GpuCase:
         return out, lse
 
 
+    def decode_mq(self, num_splits=0, with_lse=True, stream=None):
+        """All new tokens of every sequence in one multi-query decode call."""
+        c = self.case
+        B = len(c.q_lens)
+        d = self.desc()
+        L = int(c.seq_lens.max())
+        Q = int(c.q_lens.max())
+        ws_bytes = ink.inkattn_relattn_decode_mq_workspace_size(d, B, c.num_tokens, Q, L,
+                                                                num_splits)
+        ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
+        out = torch.empty_like(self.q)
+        lse = (torch.empty((c.num_tokens, c.num_q_heads), dtype=torch.float32, device="cuda")
+               if with_lse else None)
+        ink.inkattn_relattn_decode_mq(d, B, c.num_tokens, Q, L, self.q, self.k_cache,
+                                      self.v_cache, self.block_table, self.block_table.shape[1],
+                                      self.cu, self.seq_lens, self.bias, out, lse, num_splits,
+                                      ws, ws_bytes, stream)
+        return out, lse
+
+
 # ---- oracle side ----
 def oracle_sconv(case):
     return oracle.sconv_batch(case.k_pre, case.v_pre, case.conv_w, case.conv_state,

@@ -172,3 +172,40 @@ def test_probes_reject_bad_arguments():
     assert lib.inkattn_probe_stream_read(FAKE + 4, 1024, FAKE, None) == ink.EINVAL
     assert lib.inkattn_probe_stream_read(FAKE, 1000, FAKE, None) == ink.EINVAL
     assert lib.inkattn_probe_stream_read(FAKE, 1024, None, None) == ink.EINVAL
+
+
+def _decode_mq(desc, **kw):
+    args = dict(num_seqs=2, num_tokens=5, max_q_len=4, max_seq_len=100, q=FAKE, k=FAKE, v=FAKE,
+                bt=FAKE, mb=4, cu=FAKE, sl=FAKE, bias=FAKE, out=FAKE, lse=None, splits=0,
+                ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    return ink._lib._lib.inkattn_relattn_decode_mq(
+        ctypes.byref(desc), args["num_seqs"], args["num_tokens"], args["max_q_len"],
+        args["max_seq_len"], args["q"], args["k"], args["v"], args["bt"], args["mb"],
+        args["cu"], args["sl"], args["bias"], args["out"], args["lse"], args["splits"],
+        args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(max_q_len=0), 1), (dict(max_q_len=17), 2), (dict(num_tokens=1), 1),
+    (dict(cu=None), 1), (dict(q=None), 1), (dict(ws=None), 1), (dict(ws_bytes=16), 1),
+    (dict(q=FAKE + 4), 1), (dict(num_seqs=0), 0), (dict(num_tokens=0), 0),
+    (dict(num_seqs=40000, num_tokens=80000, max_q_len=4), 2),
+])
+def test_decode_mq_host_validation(kw, status):
+    d = ink.make_desc(ink.BF16, 32, 4, 0, 128)
+    assert _decode_mq(d, **kw) == status
+
+
+def test_decode_mq_splits_and_workspace():
+    d = ink.make_desc(ink.BF16, 32, 4, 4096, 4096)
+    # one token per sequence: the same heuristic as plain decode
+    assert ink.inkattn_relattn_decode_mq_num_splits(d, 64, 1, 16384) == \
+        ink.inkattn_relattn_decode_num_splits(d, 64, 16384)
+    # 9 tokens x 8 heads = 5 column tiles of 16: fewer splits fill the GPU
+    assert ink.inkattn_relattn_decode_mq_num_splits(d, 16, 9, 16384) == 1
+    assert ink.inkattn_relattn_decode_mq_num_splits(d, 2, 9, 16384) == 7
+    n = ink.inkattn_relattn_decode_mq_workspace_size(d, 2, 10, 9, 16384, 3)
+    rows = 10 * 32 * 3
+    assert n == rows * 128 * 4 + ((rows * 4 + 15) // 16) * 16
+    assert ink.inkattn_relattn_decode_mq_workspace_size(d, 2, 10, 17, 16384, 3) == 0

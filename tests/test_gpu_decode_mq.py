@@ -1,0 +1,90 @@
+"""GPU parity of inkattn_relattn_decode_mq: several query tokens per
+sequence (the verification of multi-token-prediction drafts), run after
+inkattn_sconv has written them, against the oracle's attention of those
+tokens with the sequence's earlier tokens as context."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import GpuCase, assert_close, assert_parity, host, oracle_kv, oracle_sconv
+
+pytestmark = pytest.mark.gpu
+
+
+def _expected(case):
+    k_new, v_new, _ = oracle_sconv(case)
+    G = case.num_q_heads // case.num_kv_heads
+    outs, lses = [], []
+    for b in range(len(case.q_lens)):
+        L, n = int(case.seq_lens[b]), int(case.q_lens[b])
+        lo = max(0, L - n - case.window + 1) if case.window else 0
+        K, V = oracle_kv(case, b, k_new, v_new, lo=lo)
+        t0 = int(case.cu_seqlens[b])
+        o, l = oracle.relattn_prefill(case.q[t0:t0 + n], K, V, case.bias, case.window, G)
+        outs.append(o)
+        lses.append(l)
+    return np.concatenate(outs), np.concatenate(lses)
+
+
+def _run_and_check(case, num_splits=0):
+    gc = GpuCase(case)
+    gc.sconv()
+    out, lse = gc.decode_mq(num_splits)
+    torch.cuda.synchronize()
+    want_o, want_l = _expected(case)
+    assert_parity(host(out), want_o, case.dtype, "out")
+    assert_parity(host(lse), want_l, case.dtype, "lse")
+    return gc, out, lse
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (32, 4), (16, 1)])
+@pytest.mark.parametrize("W,R", [(0, 5000), (64, 64), (300, 40)])
+def test_decode_mq_ragged(dtype, Hq, Hkv, W, R):
+    # 1..9 query tokens (one accepted token and up to 8 drafts) on contexts
+    # that put the tokens across page edges and on unaligned tails
+    q_lens = [1, 2, 9, 5, 3, 9, 7]
+    ctx = [0, 126, 119, 1000, 3, 4090, 250]
+    case = synth.make_case(dtype, q_lens, ctx, Hq, Hkv, W, R, seed=40 + Hq + W,
+                           extra_blocks=2)
+    _run_and_check(case)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 5, 40])
+def test_decode_mq_split_counts(num_splits):
+    case = synth.make_case("fp32", [4, 9, 1], [2999, 5000, 640], 32, 4, 0, 6000, seed=41)
+    _run_and_check(case, num_splits)
+
+
+def test_decode_mq_sixteen_tokens():
+    # the largest supported query count: 8 heads x 16 tokens = 8 column tiles
+    case = synth.make_case("bf16", [16, 16, 11], [130, 2000, 0], 32, 4, 512, 512, seed=42)
+    _run_and_check(case)
+
+
+def test_decode_mq_one_token_matches_decode_bitwise():
+    case = synth.make_case("bf16", [1] * 5, [4095, 4096, 333, 9000, 17], 32, 4, 2048, 2048,
+                           seed=43)
+    gc = GpuCase(case)
+    gc.sconv()
+    o1, l1 = gc.decode()
+    o2, l2 = gc.decode_mq()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_mq_matches_prefill_and_is_repeatable():
+    # the same tokens through the prefill kernel (chunk with context)
+    case = synth.make_case("fp32", [6, 2, 9], [700, 4100, 1500], 32, 4, 1024, 1024, seed=44)
+    gc = GpuCase(case)
+    gc.sconv()
+    om, lm = gc.decode_mq(3)
+    om2, lm2 = gc.decode_mq(3)
+    op, lp = gc.prefill()
+    torch.cuda.synchronize()
+    assert torch.equal(om, om2) and torch.equal(lm, lm2)
+    assert_close(host(om), host(op), 1e-5, "decode_mq vs prefill")
+    assert_close(host(lm), host(lp), 1e-5, "lse decode_mq vs prefill")
