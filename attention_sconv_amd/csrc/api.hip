@@ -64,6 +64,15 @@ bool bias_table_too_large(const inkattn_attn_desc_t* d) {
   return (uint64_t)d->num_q_heads * (uint64_t)d->bias_len * elem >= (1ull << 31);
 }
 
+// The decode grid is one dimension of (split, kv-head, sequence) x column
+// tile work-groups, with 32-bit indices inside the kernel.
+bool decode_grid_too_large(const inkattn_attn_desc_t* d, int64_t num_seqs, int64_t splits,
+                           int32_t max_q_len) {
+  const int64_t rest = splits * d->num_kv_heads * num_seqs;
+  const int64_t n_ct = inkattn::decode_column_tiles(d->num_q_heads / d->num_kv_heads, max_q_len);
+  return (rest + 7) / 8 * 8 * n_ct > 0x7fffffffLL;
+}
+
 inkattn_status_t from_hip(hipError_t e) { return e == hipSuccess ? INKATTN_OK : INKATTN_EHIP; }
 
 }  // namespace
@@ -158,7 +167,6 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
   if (num_seqs < 0 || max_seq_len < 0 || num_splits < 0) return INKATTN_EINVAL;
   if (num_seqs == 0) return INKATTN_OK;
   if (max_seq_len < 1 || max_blocks_per_seq < 1) return INKATTN_EINVAL;
-  if (num_seqs > 65535) return INKATTN_ENOTSUP;                  // one grid row per sequence
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !bias || !out || !workspace)
     return INKATTN_EINVAL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
@@ -166,6 +174,7 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
     return INKATTN_EINVAL;
   if (bias_table_too_large(desc)) return INKATTN_ENOTSUP;
   const int32_t s = num_splits == 0 ? auto_splits(desc, num_seqs, max_seq_len) : num_splits;
+  if (decode_grid_too_large(desc, num_seqs, s, 1)) return INKATTN_ENOTSUP;
   const size_t need = inkattn_relattn_decode_workspace_size(desc, num_seqs, max_seq_len, s);
   if (workspace_bytes < need) return INKATTN_EINVAL;
   const size_t rows = (size_t)num_seqs * desc->num_q_heads * (size_t)s;
@@ -216,8 +225,6 @@ inkattn_status_t inkattn_relattn_decode_mq(const inkattn_attn_desc_t* desc, int3
   if (max_q_len < 1 || num_tokens < num_seqs || max_seq_len < 1 || max_blocks_per_seq < 1)
     return INKATTN_EINVAL;
   if (max_q_len > kMaxDecodeQueries) return INKATTN_ENOTSUP;
-  const int n_ct = inkattn::decode_column_tiles(desc->num_q_heads / desc->num_kv_heads, max_q_len);
-  if ((int64_t)num_seqs * n_ct > 65535) return INKATTN_ENOTSUP;
   if (!q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !seq_lens || !bias ||
       !out || !workspace)
     return INKATTN_EINVAL;
@@ -227,6 +234,7 @@ inkattn_status_t inkattn_relattn_decode_mq(const inkattn_attn_desc_t* desc, int3
   if (bias_table_too_large(desc)) return INKATTN_ENOTSUP;
   const int32_t s =
       num_splits == 0 ? auto_splits(desc, num_seqs, max_seq_len, max_q_len) : num_splits;
+  if (decode_grid_too_large(desc, num_seqs, s, max_q_len)) return INKATTN_ENOTSUP;
   const size_t need = inkattn_relattn_decode_mq_workspace_size(desc, num_seqs, num_tokens,
                                                                max_q_len, max_seq_len, s);
   if (workspace_bytes < need) return INKATTN_EINVAL;

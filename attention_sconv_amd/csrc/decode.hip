@@ -46,7 +46,7 @@ constexpr int kDecodeThreads = 64 * kDecodeWaves;
 
 template <typename T>
 __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
-    int Hq, int Hkv, int window, int R, int S, int n_ct, const T* __restrict__ q,
+    int Hq, int Hkv, int window, int R, int S, int n_ct, int B, const T* __restrict__ q,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const T* __restrict__ bias,
@@ -56,10 +56,18 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
   __shared__ float sm_l[kDecodeWaves][16];
   __shared__ float sm_o[kDecodeWaves][16][kHeadDim + 4];
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z / n_ct;
-  const int ct = blockIdx.z % n_ct;  // column tile: columns 16ct .. 16ct+15
+  // Work-group id -> (split, kv-head, sequence, column tile).  The column
+  // tiles of one (split, kv-head, sequence) get ids 8 apart: the hardware
+  // deals ids round-robin over the 8 XCDs, so they run side by side on one
+  // XCD and all but the first read the K/V range from its L2.  With one
+  // column tile this is the plain order (split fastest).
+  const int id = blockIdx.x;
+  const int ct = (id >> 3) % n_ct;   // column tile: columns 16ct .. 16ct+15
+  const int rest = (id & 7) + 8 * ((id >> 3) / n_ct);
+  if (rest >= S * Hkv * B) return;               // (padding of the last group of 8)
+  const int split = rest % S;
+  const int kvh = (rest / S) % Hkv;
+  const int b = rest / (S * Hkv);
   const int G = Hq / Hkv;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -308,11 +316,14 @@ hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_tokens, int m
                          const int32_t* seq_lens, const void* bias, void* out, float* lse,
                          float* part_o, float* part_lse, hipStream_t stream) {
   const int n_ct = decode_column_tiles(s.Hq / s.Hkv, max_q_len);
-  dim3 grid(num_splits, s.Hkv, num_seqs * n_ct);
+  // One work-group per (split, kv-head, sequence) x column tile, in groups
+  // of 8 (see the kernel's id mapping).
+  const long rest = (long)num_splits * s.Hkv * num_seqs;
+  dim3 grid((unsigned)((rest + 7) / 8 * 8 * n_ct));
   dim3 mgrid(s.Hq, num_tokens);
   if (s.dtype == kDtypeBf16) {
     hipLaunchKernelGGL(decode_split_kernel<bf16>, grid, dim3(kDecodeThreads), 0, stream, s.Hq,
-                       s.Hkv, s.window, s.bias_len, num_splits, n_ct, (const bf16*)q,
+                       s.Hkv, s.window, s.bias_len, num_splits, n_ct, num_seqs, (const bf16*)q,
                        (const bf16*)k_cache, (const bf16*)v_cache, block_table,
                        max_blocks_per_seq, cu_seqlens_q, seq_lens, (const bf16*)bias, part_o,
                        part_lse, (bf16*)out, lse);
@@ -321,7 +332,7 @@ hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_tokens, int m
                          num_splits, part_o, part_lse, (bf16*)out, lse);
   } else {
     hipLaunchKernelGGL(decode_split_kernel<float>, grid, dim3(kDecodeThreads), 0, stream, s.Hq,
-                       s.Hkv, s.window, s.bias_len, num_splits, n_ct, (const float*)q,
+                       s.Hkv, s.window, s.bias_len, num_splits, n_ct, num_seqs, (const float*)q,
                        (const float*)k_cache, (const float*)v_cache, block_table,
                        max_blocks_per_seq, cu_seqlens_q, seq_lens, (const float*)bias, part_o,
                        part_lse, (float*)out, lse);

@@ -107,6 +107,22 @@ class DeviceCase:
                                         self.block_table.shape[1], self.seq_lens, self.bias,
                                         self.out, None, 0, self.ws, self.ws_bytes)
 
+    def setup_decode_mq(self, torch):
+        c = self.case
+        B, L, Q = len(c.q_lens), int(c.seq_lens.max()), int(c.q_lens.max())
+        self.num_splits = self.ink.inkattn_relattn_decode_mq_num_splits(self.desc, B, Q, L)
+        self.ws_bytes = self.ink.inkattn_relattn_decode_mq_workspace_size(
+            self.desc, B, c.num_tokens, Q, L, 0)
+        self.ws = torch.empty(self.ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
+
+    def decode_mq(self):
+        c = self.case
+        self.ink.inkattn_relattn_decode_mq(self.desc, len(c.q_lens), c.num_tokens,
+                                           int(c.q_lens.max()), int(c.seq_lens.max()), self.q,
+                                           self.k_cache, self.v_cache, self.block_table,
+                                           self.block_table.shape[1], self.cu, self.seq_lens,
+                                           self.bias, self.out, None, 0, self.ws, self.ws_bytes)
+
 
 def recorded_traffic(profile, sources):
     """HBM bytes per launch recorded by the rocprofv3 FETCH_SIZE/WRITE_SIZE
@@ -370,6 +386,43 @@ def main():
             "note": "achieved/frac: back-to-back steps; flushed: L2/MALL evicted before each step",
         }
         del dd
+        torch.cuda.empty_cache()
+
+        # ---------------- MTP verification: 9 query tokens per sequence
+        mwl = synth.WORKLOADS["swa_decode_16k_mtp9"]
+        mcase = synth.workload_case(mwl, seed=0, past_device="cuda")
+        md = DeviceCase(mcase, torch)
+        md.setup_decode_mq(torch)
+        m_keys = min(mwl.window + mwl.q_len - 1, mwl.seq_len)
+        m_kv_bytes = mwl.batch * mwl.num_kv_heads * 2 * m_keys * HEAD_DIM * 2
+        m_pairs = sum(valid_pairs(mwl.q_len, mwl.seq_len, mwl.window)
+                      for _ in range(mwl.batch)) * mwl.num_q_heads
+
+        def mstep(ev):
+            md.sconv()
+            if ev is not None:
+                ev[0].record()
+            md.decode_mq()
+            if ev is not None:
+                ev[1].record()
+
+        print(f"[bench] decode {mwl.name}", file=sys.stderr, flush=True)
+        steady_clocks(torch, mstep, args.steady_s)
+        m_ms_step, mks = time_region(torch, mstep, None, d_steps, args.warmup)
+        m_ms = sum(mks) / len(mks)
+        m_gbs = m_kv_bytes / (m_ms * 1e-3) / 1e9
+        result["decode_mtp"] = {
+            "workload": mwl.name + ": " + mwl.description,
+            "ms_decode": round(m_ms, 4), "ms_decode_median": round(float(np.median(mks)), 4),
+            "num_splits": md.num_splits, "kv_bytes": m_kv_bytes,
+            "achieved": round(m_gbs, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
+            "frac": round(m_gbs / PEAK_HBM_GBS, 4),
+            "tflops": round(4 * HEAD_DIM * m_pairs / (m_ms * 1e-3) / 1e12, 2),
+            "time_vs_one_token_decode": round(m_ms / d_ms, 3),
+            "note": "inkattn_relattn_decode_mq; the 9 tokens of a sequence read its K/V once "
+                    "per 16 (token, head) columns",
+        }
+        del md
 
     import attention_sconv_amd as ink
     print("[bench] measured ceilings", file=sys.stderr, flush=True)

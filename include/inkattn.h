@@ -157,7 +157,8 @@ size_t inkattn_relattn_decode_workspace_size(const inkattn_attn_desc_t* desc,
  *   num_splits : 0 = auto (inkattn_relattn_decode_num_splits), else >= 1.
  *   workspace  : device memory of at least
  *                inkattn_relattn_decode_workspace_size(...) bytes, 16 B aligned.
- * INKATTN_ENOTSUP if the bias table (Hq * R elements) reaches 2 GiB. */
+ * INKATTN_ENOTSUP if the bias table (Hq * R elements) reaches 2 GiB, or if
+ * num_splits * Hkv * num_seqs work-groups exceed 2^31. */
 inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t num_seqs,
                                         int32_t max_seq_len, const void* q,
                                         const void* k_cache, const void* v_cache,
@@ -185,8 +186,7 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
  *   workspace: device, 16-byte aligned, >= inkattn_relattn_decode_mq_
  *              workspace_size(...) bytes; caller-owned scratch.
  *   num_splits: 0 = automatic (inkattn_relattn_decode_mq_num_splits).
- * Errors as inkattn_relattn_decode; INKATTN_ENOTSUP for max_q_len > 16 or
- * num_seqs * ceil(Hq/Hkv * max_q_len / 16) > 65535. */
+ * Errors as inkattn_relattn_decode; INKATTN_ENOTSUP for max_q_len > 16. */
 int32_t inkattn_relattn_decode_mq_num_splits(const inkattn_attn_desc_t* desc, int32_t num_seqs,
                                              int32_t max_q_len, int32_t max_seq_len);
 size_t inkattn_relattn_decode_mq_workspace_size(const inkattn_attn_desc_t* desc,

@@ -78,6 +78,10 @@ WORKLOADS = {
     "swa_decode_16k": Workload(
         "swa_decode_16k", "decode", "bf16", 64, 16384, 1, 32, 4, 4096, 4096,
         description="batch 64, L=16384, window 4096, R=4096, Hq=32, Hkv=4, bf16"),
+    "swa_decode_16k_mtp9": Workload(
+        "swa_decode_16k_mtp9", "decode", "bf16", 64, 16384, 9, 32, 4, 4096, 4096,
+        description="batch 64, L=16384 with the last 9 tokens (1 accepted + 8 MTP drafts) "
+                    "as queries, window 4096, R=4096, Hq=32, Hkv=4, bf16"),
     "full_decode_1m": Workload(
         "full_decode_1m", "decode", "bf16", 4, 1048576, 1, 32, 4, 0, 1048576,
         description="batch 4, L=1,048,576, full causal, R=1,048,576, Hq=32, "
@@ -202,6 +206,6 @@ def workload_case(wl: Workload, seed=0, past_device=None, batch=None):
         return make_case(wl.dtype, [wl.q_len] * B, [wl.seq_len - wl.q_len] * B,
                          wl.num_q_heads, wl.num_kv_heads, wl.window, wl.bias_len,
                          seed=seed, past_device=past_device)
-    return make_case(wl.dtype, [1] * B, [wl.seq_len - 1] * B, wl.num_q_heads,
+    return make_case(wl.dtype, [wl.q_len] * B, [wl.seq_len - wl.q_len] * B, wl.num_q_heads,
                      wl.num_kv_heads, wl.window, wl.bias_len, seed=seed,
                      past_device=past_device)

@@ -190,7 +190,7 @@ def _decode_mq(desc, **kw):
     (dict(max_q_len=0), 1), (dict(max_q_len=17), 2), (dict(num_tokens=1), 1),
     (dict(cu=None), 1), (dict(q=None), 1), (dict(ws=None), 1), (dict(ws_bytes=16), 1),
     (dict(q=FAKE + 4), 1), (dict(num_seqs=0), 0), (dict(num_tokens=0), 0),
-    (dict(num_seqs=40000, num_tokens=80000, max_q_len=4), 2),
+    (dict(num_seqs=1000, num_tokens=2000, splits=1 << 20), 2),     # grid beyond 2^31 groups
 ])
 def test_decode_mq_host_validation(kw, status):
     d = ink.make_desc(ink.BF16, 32, 4, 0, 128)
