@@ -265,6 +265,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-mtp", action="store_true",
+                    help="skip the MTP-verification decode leg (it launches the decode kernel "
+                         "with another shape)")
     ap.add_argument("--steady-s", type=float, default=0.3,
                     help="seconds of untimed back-to-back steps before the warmup steps, "
                          "so that the timed steps run at the sustained shader clock")
@@ -388,7 +391,8 @@ def main():
         del dd
         torch.cuda.empty_cache()
 
-        # ---------------- MTP verification: 9 query tokens per sequence
+    # ---------------- MTP verification: 9 query tokens per sequence
+    if not args.no_decode and not args.no_mtp:
         mwl = synth.WORKLOADS["swa_decode_16k_mtp9"]
         mcase = synth.workload_case(mwl, seed=0, past_device="cuda")
         md = DeviceCase(mcase, torch)
