@@ -144,3 +144,13 @@ def test_tiny_fp32_prefill_then_decode_against_oracle():
     torch.cuda.synchronize()
     assert_parity(host(torch.cat(outs)), want, "fp32", "prefill + decode outputs")
     assert_parity(host(torch.cat(lses)), want_lse, "fp32", "prefill + decode lse")
+
+
+@pytest.mark.parametrize("W,R", [(1, 1), (1, 300), (129, 1)])
+def test_decode_window_and_table_edges(W, R):
+    # a window of only the new token, a one-entry bias table, a window one
+    # key past a page
+    L = [1, 128, 129, 4097]
+    case = synth.make_case("bf16", [1] * len(L), [x - 1 for x in L], 32, 4, W, R,
+                           seed=23 + W + R)
+    _run_and_check(case)

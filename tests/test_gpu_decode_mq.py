@@ -88,3 +88,11 @@ def test_decode_mq_matches_prefill_and_is_repeatable():
     assert torch.equal(om, om2) and torch.equal(lm, lm2)
     assert_close(host(om), host(op), 1e-5, "decode_mq vs prefill")
     assert_close(host(lm), host(lp), 1e-5, "lse decode_mq vs prefill")
+
+
+@pytest.mark.parametrize("W,R", [(1, 1), (2, 7), (9, 1)])
+def test_decode_mq_small_windows(W, R):
+    # windows shorter than the run of query tokens: early tokens' keys drop out
+    # of later tokens' windows inside the same call
+    case = synth.make_case("bf16", [9, 9, 4], [0, 300, 128], 32, 4, W, R, seed=45 + W)
+    _run_and_check(case)

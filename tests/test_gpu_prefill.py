@@ -12,9 +12,11 @@ from gpu_util import GpuCase, assert_close, assert_parity, host, oracle_kv, orac
 pytestmark = pytest.mark.gpu
 
 
-def _expected(case, rows_per_seq=None):
+def _expected(case, rows_per_seq=None, stored_kv=False):
     """Oracle output for the chosen chunk rows of every sequence; returns
-    (token indices, out [n, Hq, d], lse [n, Hq])."""
+    (token indices, out [n, Hq, d], lse [n, Hq]).  With ``stored_kv`` (bf16
+    cases) the oracle reads the post-convolution K/V as the cache stores them,
+    rounded to bf16, instead of in fp64."""
     k_new, v_new, _ = oracle_sconv(case)
     G = case.num_q_heads // case.num_kv_heads
     toks, outs, lses = [], [], []
@@ -23,6 +25,9 @@ def _expected(case, rows_per_seq=None):
         rows = np.arange(qn) if rows_per_seq is None else np.asarray(rows_per_seq(b, qn))
         t0 = int(case.cu_seqlens[b])
         K, V = oracle_kv(case, b, k_new, v_new)
+        if stored_kv and case.dtype == "bf16":
+            K = synth.round_bf16(K.astype(np.float32)).astype(np.float64)
+            V = synth.round_bf16(V.astype(np.float32)).astype(np.float64)
         o, l = oracle.relattn_prefill(case.q[t0:t0 + qn], K, V, case.bias, case.window, G,
                                       rows=rows)
         toks.append(t0 + rows)
@@ -31,12 +36,12 @@ def _expected(case, rows_per_seq=None):
     return np.concatenate(toks), np.concatenate(outs), np.concatenate(lses)
 
 
-def _run_and_check(case, rows_per_seq=None):
+def _run_and_check(case, rows_per_seq=None, stored_kv=False):
     gc = GpuCase(case)
     gc.sconv()
     out, lse = gc.prefill()
     torch.cuda.synchronize()
-    toks, want_o, want_l = _expected(case, rows_per_seq)
+    toks, want_o, want_l = _expected(case, rows_per_seq, stored_kv)
     assert_parity(host(out)[toks], want_o, case.dtype, "out")
     assert_parity(host(lse)[toks], want_l, case.dtype, "lse")
     return gc, out, lse
@@ -153,3 +158,21 @@ def test_prefill_full_32k_full_size_sampled():
     wl = synth.WORKLOADS["full_prefill_32k"]
     case = synth.workload_case(wl, seed=0)
     _run_and_check(case, rows_per_seq=lambda b, n: _sample_rows(n, 7 + b))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv", [(16, 1), (32, 4)])
+@pytest.mark.parametrize("W,R", [(1, 1), (1, 50), (2, 1), (256, 1), (257, 3000), (100000, 64)])
+def test_prefill_window_and_table_edges(dtype, Hq, Hkv, W, R):
+    # a window of one key (only the diagonal), a bias table of one entry (a
+    # constant per head), windows at and just past the 256-row query tile, and
+    # a window longer than every sequence; queries span several query tiles.
+    # With a window of two keys an output is a two-point interpolation whose
+    # weight moves with the rounding of the stored keys by more than the bf16
+    # bound allows, so the bf16 cases compare against the oracle on the keys
+    # and values as the cache stores them (rounded to bf16).
+    q_lens = [1, 2, 255, 256, 257, 600]
+    ctx = [0, 3, 0, 130, 7, 0]
+    case = synth.make_case(dtype, q_lens, ctx, Hq, Hkv, W, R, seed=70 + W % 97 + R % 13,
+                           extra_blocks=1)
+    _run_and_check(case, stored_kv=True)
