@@ -34,6 +34,8 @@
 //
 // Merge kernel: per (sequence, q-head), lse = log sum_s exp(lse_s) and
 // out = sum_s exp(lse_s - lse) o_s; splits that saw no key have lse = -inf.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -41,29 +43,35 @@ namespace inkattn {
 
 namespace {
 
-constexpr int kDecodeWaves = 8;
-constexpr int kDecodeThreads = 64 * kDecodeWaves;
+// Column tiles one 4-wave bf16 work-group carries (three fit its registers
+// with the double-buffered K/V: 256 VGPRs and ~226 AGPRs; four spill).
+constexpr int kMaxTilesPerGroup = 3;
 
-template <typename T>
-__global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
-    int Hq, int Hkv, int window, int R, int S, int n_ct, int B, const T* __restrict__ q,
+// kW waves per work-group; kCT column tiles of 16 per work-group.  Plain
+// decode and fp32 use <8, 1>.  bf16 with several tiles uses 4 waves (one per
+// SIMD, so a wave may hold up to 512 registers) and keeps every tile's state
+// in the same wave, so each K/V fragment it loads serves all of its tiles.
+template <typename T, int kW, int kCT>
+__global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
+    int Hq, int Hkv, int window, int R, int S, int n_cg, int B, const T* __restrict__ q,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const T* __restrict__ bias,
     float* __restrict__ part_o, float* __restrict__ part_lse, T* __restrict__ out,
     float* __restrict__ lse) {
-  __shared__ float sm_m[kDecodeWaves][16];
-  __shared__ float sm_l[kDecodeWaves][16];
-  __shared__ float sm_o[kDecodeWaves][16][kHeadDim + 4];
+  constexpr int kThr = 64 * kW;
+  __shared__ float sm_m[kW][16];
+  __shared__ float sm_l[kW][16];
+  __shared__ float sm_o[kW][16][kHeadDim + 4];
 
-  // Work-group id -> (split, kv-head, sequence, column tile).  The column
-  // tiles of one (split, kv-head, sequence) get ids 8 apart: the hardware
+  // Work-group id -> (split, kv-head, sequence, column group).  The column
+  // groups of one (split, kv-head, sequence) get ids 8 apart: the hardware
   // deals ids round-robin over the 8 XCDs, so they run side by side on one
   // XCD and all but the first read the K/V range from its L2.  With one
-  // column tile this is the plain order (split fastest).
+  // column group this is the plain order (split fastest).
   const int id = blockIdx.x;
-  const int ct = (id >> 3) % n_ct;   // column tile: columns 16ct .. 16ct+15
-  const int rest = (id & 7) + 8 * ((id >> 3) / n_ct);
+  const int cgi = (id >> 3) % n_cg;  // column group: tiles kCT*cgi .. kCT*cgi+kCT-1
+  const int rest = (id & 7) + 8 * ((id >> 3) / n_cg);
   if (rest >= S * Hkv * B) return;               // (padding of the last group of 8)
   const int split = rest % S;
   const int kvh = (rest / S) % Hkv;
@@ -76,12 +84,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
 
   // The query tokens of sequence b (one for plain decode; up to a few draft
   // tokens when several positions are verified at once) sit at positions
-  // L-q_len .. L-1.  Column c of the work-group's tiles is (token c / G,
-  // head c % G of the group); this work-group computes columns 16ct .. +15.
+  // L-q_len .. L-1.  Column c of a kv-head group is (token c / G, head
+  // c % G); column tile t holds columns 16t .. 16t+15.
   const int tok0 = cu_q != nullptr ? cu_q[b] : b;
   const int q_len = cu_q != nullptr ? cu_q[b + 1] - tok0 : 1;
   const int n_cols = G * q_len;
-  if (16 * ct >= n_cols) return;                 // (wave-uniform: the whole work-group)
+  if (16 * kCT * cgi >= n_cols) return;          // (wave-uniform: the whole work-group)
   const int L = seq_lens[b];
   const int pos0 = L - q_len;                    // position of the first query token
   const int kstart = window > 0 ? max(0, pos0 - window + 1) : 0;
@@ -93,29 +101,37 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
   const int my_hi = min(my_lo + bps, blk_last + 1);
   const int n_items = 4 * max(my_hi - my_lo, 0);   // item i: page my_lo + i/4, keys 32(i%4) ..
 
-  const int gc = 16 * ct + col;
-  const bool head_ok = gc < n_cols;             // this lane's column is a real (token, head)
-  const int token = head_ok ? gc / G : 0;
-  const int h = kvh * G + (head_ok ? gc % G : 0);
-  const int pos = pos0 + token;                  // this column's query position
-  const int k_lo = window > 0 ? max(0, pos - window + 1) : 0;    // its visible keys: k_lo .. pos
-  Frag8<T> qf[4];
-#pragma unroll
-  for (int ds = 0; ds < 4; ++ds)
-    qf[ds] = head_ok ? Frag8<T>::load(q + ((size_t)(tok0 + token) * Hq + h) * kHeadDim + 32 * ds +
-                                      8 * grp)
-                     : Frag8<T>::zero();
-  // Bias row of this lane's head, as an element index into the whole table
-  // (the entry point keeps the table under 2 GiB).
+  // Per column tile u of this work-group: this lane's column, its query
+  // position and visible keys k_lo .. pos, its bias row (an element index
+  // into the whole table, which the entry point keeps under 2 GiB), its Q^T
+  // fragments and running softmax state.
   const rsrc_t bias_r = make_rsrc(bias, (uint32_t)((size_t)Hq * R * sizeof(T)));
-  const uint32_t bias_row = (uint32_t)h * (uint32_t)R;
-
-  const float c = 0.08838834764831845f * kLog2e;   // log2(e) / sqrt(128)
-  float m = -INFINITY;                             // running max (log2 units)
-  float l = 0.0f;                                  // this lane's share of the sum
-  f32x4 o[8];
+  bool head_ok[kCT];
+  int pos[kCT], k_lo[kCT];
+  uint32_t bias_row[kCT];
+  Frag8<T> qf[kCT][4];
+  float m[kCT], l[kCT];                          // running max (log2 units), this lane's sum
+  f32x4 o[kCT][8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0, 0, 0, 0};
+  for (int u = 0; u < kCT; ++u) {
+    const int gc = 16 * (kCT * cgi + u) + col;
+    head_ok[u] = gc < n_cols;
+    const int token = head_ok[u] ? gc / G : 0;
+    const int h = kvh * G + (head_ok[u] ? gc % G : 0);
+    pos[u] = pos0 + token;
+    k_lo[u] = window > 0 ? max(0, pos[u] - window + 1) : 0;
+    bias_row[u] = (uint32_t)h * (uint32_t)R;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      qf[u][ds] = head_ok[u] ? Frag8<T>::load(q + ((size_t)(tok0 + token) * Hq + h) * kHeadDim +
+                                              32 * ds + 8 * grp)
+                             : Frag8<T>::zero();
+    m[u] = -INFINITY;
+    l[u] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[u][dt] = f32x4{0, 0, 0, 0};
+  }
+  const float c = 0.08838834764831845f * kLog2e;   // log2(e) / sqrt(128)
 
   auto page_base = [&](int blk) -> size_t {
     const int phys = block_table[(size_t)b * max_blocks + blk];
@@ -125,22 +141,26 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
   // of the page, so accumulator register r of lane group G in tile t holds
   // key 32u + 8G + 4t + r.
   // Everything an item needs is loaded in one batch, one item ahead: K and
-  // V^T fragments and the 8 bias entries of this lane's keys.  Bias indices
-  // are clamped into the table (masked keys are dropped later by a select),
-  // so no load sits behind a branch and no wait drains the prefetch.
+  // V^T fragments and, per column tile, the 8 bias entries of this lane's
+  // keys.  Bias indices are clamped into the table (masked keys are dropped
+  // later by a select), so no load sits behind a branch and no wait drains
+  // the prefetch.
   // Each page is read through a buffer descriptor of its own; the quarter
   // and the dim tile are wave-uniform offsets, so the only per-lane address
   // state is one fixed byte offset for K and one for V^T.
   constexpr uint32_t kPageBytes = kPage * kHeadDim * sizeof(T);
   const uint32_t k_lane = ((8 * (col >> 2) + (col & 3)) * kHeadDim + 8 * grp) * sizeof(T);
   const uint32_t v_lane = (col * kPage + 8 * grp) * sizeof(T);
-  auto load_item = [&](int item, Frag8<T>* kf, Frag8<T>* vf, T* bb) {
+  auto load_item = [&](int item, Frag8<T>* kf, Frag8<T>* vf, T (*bb)[8]) {
     const int blk = my_lo + (item >> 2);
-    const int u = item & 3;
-    const int j0 = blk * kPage + 32 * u + 8 * grp;
+    const int qu = item & 3;
+    const int j0 = blk * kPage + 32 * qu + 8 * grp;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      bb[e] = buf_load_elem<T>(bias_r, (bias_row + min(max(pos - (j0 + e), 0), R - 1)) * sizeof(T));
+    for (int u = 0; u < kCT; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        bb[u][e] = buf_load_elem<T>(
+            bias_r, (bias_row[u] + min(max(pos[u] - (j0 + e), 0), R - 1)) * sizeof(T));
     const size_t base = page_base(blk);
     const rsrc_t kr = make_rsrc(k_cache + base, kPageBytes);
     const rsrc_t vr = make_rsrc(v_cache + base, kPageBytes);
@@ -149,62 +169,67 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds)
         kf[t * 4 + ds] = Frag8<T>::load(kr, k_lane + (4 * t * kHeadDim + 32 * ds) * sizeof(T),
-                                        32 * u * kHeadDim * sizeof(T));
+                                        32 * qu * kHeadDim * sizeof(T));
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-      vf[dt] = Frag8<T>::load(vr, v_lane, (32 * u + 16 * dt * kPage) * sizeof(T));
+      vf[dt] = Frag8<T>::load(vr, v_lane, (32 * qu + 16 * dt * kPage) * sizeof(T));
   };
 
-  // One item of 32 keys: scores, online softmax, O^T += V^T P^T.
-  auto process_item = [&](int item, const Frag8<T>* kf, Frag8<T>* vf, const T* bb) {
+  // One item of 32 keys, for every column tile: scores, online softmax,
+  // O^T += V^T P^T.
+  auto process_item = [&](int item, const Frag8<T>* kf, Frag8<T>* vf, const T (*bb)[8]) {
     const int blk = my_lo + (item >> 2);
     const int j0 = blk * kPage + 32 * (item & 3) + 8 * grp;
-    f32x4 sacc[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sacc[t] = f32x4{0, 0, 0, 0};
+    for (int u = 0; u < kCT; ++u) {
+      f32x4 sacc[2];
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) sacc[t] = mfma16(kf[t * 4 + ds], qf[ds], sacc[t]);
-    }
+      for (int t = 0; t < 2; ++t) {
+        sacc[t] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) sacc[t] = mfma16(kf[t * 4 + ds], qf[u][ds], sacc[t]);
+      }
 
-    float x[8];
-    float mx = -INFINITY;
+      float x[8];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = j0 + e;
-      const bool ok = head_ok && j >= k_lo && j <= pos;
-      x[e] = ok ? sacc[e >> 2][e & 3] * c + to_f32(bb[e]) * kLog2e : -INFINITY;
-      mx = fmaxf(mx, x[e]);
-    }
-    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m, mx);
-    const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = fast_exp2(m - m_sub);       // m = -inf -> 0
-    float p[8];
-    float psum = 0.0f;
+      for (int e = 0; e < 8; ++e) {
+        const int j = j0 + e;
+        const bool ok = head_ok[u] && j >= k_lo[u] && j <= pos[u];
+        x[e] = ok ? sacc[e >> 2][e & 3] * c + to_f32(bb[u][e]) * kLog2e : -INFINITY;
+        mx = fmaxf(mx, x[e]);
+      }
+      mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m[u], mx);
+      const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = fast_exp2(m[u] - m_sub);       // m = -inf -> 0
+      float p[8];
+      float psum = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = fast_exp2(x[e] - m_sub);
-      psum += p[e];
-    }
-    l = l * alpha + psum;
-    m = m_new;
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(x[e] - m_sub);
+        psum += p[e];
+      }
+      l[u] = l[u] * alpha + psum;
+      m[u] = m_new;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < 8; ++dt) o[u][dt] *= alpha;
 
-    const Frag8<T> pf = Frag8<T>::pack(p);
-    // Keys >= L of the last page hold no data (possibly NaN): zero them in V
-    // so that 0 * garbage cannot reach O.  The branch is wave-uniform; the
-    // per-lane part is a select, never a divergent branch around the MFMA
-    // (matrix instructions must run with every lane active).
-    if (blk == blk_last && (L & (kPage - 1)) != 0) {
-      const int nvalid = L - j0;
+      const Frag8<T> pf = Frag8<T>::pack(p);
+      // Keys >= L of the last page hold no data (possibly NaN): zero them in
+      // V (once, before the first tile's product) so that 0 * garbage cannot
+      // reach O.  The branch is wave-uniform; the per-lane part is a select,
+      // never a divergent branch around the MFMA (matrix instructions must
+      // run with every lane active).
+      if (u == 0 && blk == blk_last && (L & (kPage - 1)) != 0) {
+        const int nvalid = L - j0;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) vf[dt] = vf[dt].keep_first(nvalid);
+        for (int dt = 0; dt < 8; ++dt) vf[dt] = vf[dt].keep_first(nvalid);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[u][dt] = mfma16(vf[dt], pf, o[u][dt]);
     }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = mfma16(vf[dt], pf, o[dt]);
   };
 
   // A wave's items alternate between two register sets, so the next item's
@@ -217,10 +242,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
   // for a round that does not exist.  The barrier carries no memory fence:
   // it only holds waves together, it does not wait for their loads.
   Frag8<T> ka[8], va[8], kb[8], vb[8];
-  T ba[8], bbb[8];
-  const int rounds = (n_items + kDecodeWaves - 1) / kDecodeWaves;
-  auto item_of = [&](int r) { return min(r * kDecodeWaves + wave, n_items - 1); };
-  auto has_item = [&](int r) { return r * kDecodeWaves + wave < n_items; };
+  T ba[kCT][8], bbb[kCT][8];
+  const int rounds = (n_items + kW - 1) / kW;
+  auto item_of = [&](int r) { return min(r * kW + wave, n_items - 1); };
+  auto has_item = [&](int r) { return r * kW + wave < n_items; };
   if (rounds > 0) load_item(item_of(0), ka, va, ba);
   int r = 0;
   for (; r + 2 < rounds; r += 2) {
@@ -238,49 +263,56 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(
     process_item(item_of(r), ka, va, ba);
   }
 
-  // Merge the eight waves.  O^T register r of tile dt is dim 16dt + 4G + r.
-  float lt = l + wave_shfl_xor(l, 16);
-  lt = pair_sum(lt);
-  if (grp == 0) {
-    sm_m[wave][col] = m;
-    sm_l[wave][col] = lt;
-  }
+  // Merge the waves, one column tile at a time.  O^T register r of tile dt
+  // is dim 16dt + 4G + r.
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int u = 0; u < kCT; ++u) {
+    const int ct = kCT * cgi + u;
+    if (16 * ct >= n_cols) break;                // (wave-uniform)
+    if (u > 0) __syncthreads();                  // the previous tile's merge is done with LDS
+    float lt = l[u] + wave_shfl_xor(l[u], 16);
+    lt = pair_sum(lt);
+    if (grp == 0) {
+      sm_m[wave][col] = m[u];
+      sm_l[wave][col] = lt;
+    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm_o[wave][col][16 * dt + 4 * grp + r] = o[dt][r];
-  __syncthreads();
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sm_o[wave][col][16 * dt + 4 * grp + rr] = o[u][dt][rr];
+    __syncthreads();
 
-  const int tile_cols = min(16, n_cols - 16 * ct);
-  for (int idx = threadIdx.x; idx < tile_cols * kHeadDim; idx += kDecodeThreads) {
-    const int hh = idx / kHeadDim;               // column within the tile
-    const int d = idx % kHeadDim;
-    const int cg = 16 * ct + hh;
-    const size_t orow = (size_t)(tok0 + cg / G) * Hq + kvh * G + cg % G;
-    float M = -INFINITY;
+    const int tile_cols = min(16, n_cols - 16 * ct);
+    for (int idx = threadIdx.x; idx < tile_cols * kHeadDim; idx += kThr) {
+      const int hh = idx / kHeadDim;             // column within the tile
+      const int d = idx % kHeadDim;
+      const int cg = 16 * ct + hh;
+      const size_t orow = (size_t)(tok0 + cg / G) * Hq + kvh * G + cg % G;
+      float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm_m[w][hh]);
-    const size_t row = orow * S + split;
-    if (M == -INFINITY) {
-      part_o[row * kHeadDim + d] = 0.0f;
-      if (d == 0) part_lse[row] = -INFINITY;
-      continue;
-    }
-    float num = 0.0f, den = 0.0f;
+      for (int w = 0; w < kW; ++w) M = fmaxf(M, sm_m[w][hh]);
+      const size_t row = orow * S + split;
+      if (M == -INFINITY) {
+        part_o[row * kHeadDim + d] = 0.0f;
+        if (d == 0) part_lse[row] = -INFINITY;
+        continue;
+      }
+      float num = 0.0f, den = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float sc = fast_exp2(sm_m[w][hh] - M);
-      num += sc * sm_o[w][hh][d];
-      den += sc * sm_l[w][hh];
-    }
-    if (S == 1) {
-      // A single split is the whole key range: write the result directly
-      // (no merge pass).
-      out[orow * kHeadDim + d] = from_f32<T>(num / den);
-      if (lse != nullptr && d == 0) lse[orow] = (M + fast_log2(den)) * kLn2;
-    } else {
-      part_o[row * kHeadDim + d] = num / den;
-      if (d == 0) part_lse[row] = (M + fast_log2(den)) * kLn2;
+      for (int w = 0; w < kW; ++w) {
+        const float sc = fast_exp2(sm_m[w][hh] - M);
+        num += sc * sm_o[w][hh][d];
+        den += sc * sm_l[w][hh];
+      }
+      if (S == 1) {
+        // A single split is the whole key range: write the result directly
+        // (no merge pass).
+        out[orow * kHeadDim + d] = from_f32<T>(num / den);
+        if (lse != nullptr && d == 0) lse[orow] = (M + fast_log2(den)) * kLn2;
+      } else {
+        part_o[row * kHeadDim + d] = num / den;
+        if (d == 0) part_lse[row] = (M + fast_log2(den)) * kLn2;
+      }
     }
   }
 }
@@ -309,6 +341,29 @@ __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(
 
 }  // namespace
 
+template <typename T, int kW, int kCT>
+void launch_split(const AttnShape& s, int num_seqs, int num_splits, int n_cg, const void* q,
+                  const void* k_cache, const void* v_cache, const int32_t* block_table,
+                  int max_blocks_per_seq, const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                  const void* bias, void* out, float* lse, float* part_o, float* part_lse,
+                  hipStream_t stream) {
+  // One work-group per (split, kv-head, sequence) x column group, in groups
+  // of 8 (see the kernel's id mapping).
+  const long rest = (long)num_splits * s.Hkv * num_seqs;
+  hipLaunchKernelGGL((decode_split_kernel<T, kW, kCT>), dim3((unsigned)((rest + 7) / 8 * 8 * n_cg)),
+                     dim3(64 * kW), 0, stream, s.Hq, s.Hkv, s.window, s.bias_len, num_splits,
+                     n_cg, num_seqs, (const T*)q, (const T*)k_cache, (const T*)v_cache,
+                     block_table, max_blocks_per_seq, cu_seqlens_q, seq_lens, (const T*)bias,
+                     part_o, part_lse, (T*)out, lse);
+}
+
+template <typename T>
+void launch_merge(const AttnShape& s, int num_tokens, int num_splits, float* part_o,
+                  float* part_lse, void* out, float* lse, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_merge_kernel<T>, dim3(s.Hq, num_tokens), dim3(kHeadDim), 0, stream,
+                     s.Hq, num_splits, part_o, part_lse, (T*)out, lse);
+}
+
 hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_tokens, int max_q_len,
                          int num_splits, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* block_table,
@@ -316,29 +371,32 @@ hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_tokens, int m
                          const int32_t* seq_lens, const void* bias, void* out, float* lse,
                          float* part_o, float* part_lse, hipStream_t stream) {
   const int n_ct = decode_column_tiles(s.Hq / s.Hkv, max_q_len);
-  // One work-group per (split, kv-head, sequence) x column tile, in groups
-  // of 8 (see the kernel's id mapping).
-  const long rest = (long)num_splits * s.Hkv * num_seqs;
-  dim3 grid((unsigned)((rest + 7) / 8 * 8 * n_ct));
-  dim3 mgrid(s.Hq, num_tokens);
   if (s.dtype == kDtypeBf16) {
-    hipLaunchKernelGGL(decode_split_kernel<bf16>, grid, dim3(kDecodeThreads), 0, stream, s.Hq,
-                       s.Hkv, s.window, s.bias_len, num_splits, n_ct, num_seqs, (const bf16*)q,
-                       (const bf16*)k_cache, (const bf16*)v_cache, block_table,
-                       max_blocks_per_seq, cu_seqlens_q, seq_lens, (const bf16*)bias, part_o,
-                       part_lse, (bf16*)out, lse);
-    if (num_splits > 1)
-      hipLaunchKernelGGL(decode_merge_kernel<bf16>, mgrid, dim3(kHeadDim), 0, stream, s.Hq,
-                         num_splits, part_o, part_lse, (bf16*)out, lse);
+    if (n_ct == 1) {
+      launch_split<bf16, 8, 1>(s, num_seqs, num_splits, 1, q, k_cache, v_cache, block_table,
+                               max_blocks_per_seq, cu_seqlens_q, seq_lens, bias, out, lse,
+                               part_o, part_lse, stream);
+    } else {
+      // Several column tiles: up to kMaxTilesPerGroup per work-group, spread
+      // evenly over the fewest groups.
+      const int n_cg = (n_ct + kMaxTilesPerGroup - 1) / kMaxTilesPerGroup;
+      const int per = (n_ct + n_cg - 1) / n_cg;
+      auto go = [&](auto tag) {
+        constexpr int kCT = decltype(tag)::value;
+        launch_split<bf16, 4, kCT>(s, num_seqs, num_splits, n_cg, q, k_cache, v_cache,
+                                   block_table, max_blocks_per_seq, cu_seqlens_q, seq_lens,
+                                   bias, out, lse, part_o, part_lse, stream);
+      };
+      static_assert(kMaxTilesPerGroup == 3, "instantiations below");
+      if (per == 2) go(std::integral_constant<int, 2>{});
+      else go(std::integral_constant<int, 3>{});
+    }
+    if (num_splits > 1) launch_merge<bf16>(s, num_tokens, num_splits, part_o, part_lse, out, lse, stream);
   } else {
-    hipLaunchKernelGGL(decode_split_kernel<float>, grid, dim3(kDecodeThreads), 0, stream, s.Hq,
-                       s.Hkv, s.window, s.bias_len, num_splits, n_ct, num_seqs, (const float*)q,
-                       (const float*)k_cache, (const float*)v_cache, block_table,
-                       max_blocks_per_seq, cu_seqlens_q, seq_lens, (const float*)bias, part_o,
-                       part_lse, (float*)out, lse);
-    if (num_splits > 1)
-      hipLaunchKernelGGL(decode_merge_kernel<float>, mgrid, dim3(kHeadDim), 0, stream, s.Hq,
-                         num_splits, part_o, part_lse, (float*)out, lse);
+    launch_split<float, 8, 1>(s, num_seqs, num_splits, n_ct, q, k_cache, v_cache, block_table,
+                              max_blocks_per_seq, cu_seqlens_q, seq_lens, bias, out, lse, part_o,
+                              part_lse, stream);
+    if (num_splits > 1) launch_merge<float>(s, num_tokens, num_splits, part_o, part_lse, out, lse, stream);
   }
   return hipGetLastError();
 }
