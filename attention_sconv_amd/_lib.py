@@ -19,6 +19,7 @@ FP32, BF16 = 0, 1
 
 EXPORTED = (
     "inkattn_sconv",
+    "inkattn_sconv_paged",
     "inkattn_relattn_prefill",
     "inkattn_relattn_decode_num_splits",
     "inkattn_relattn_decode_workspace_size",
@@ -62,6 +63,9 @@ def _load():
     lib.inkattn_sconv.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                   vp, vp, vp]
     lib.inkattn_sconv.restype = i32
+    lib.inkattn_sconv_paged.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                        i32, vp, vp, vp, vp, vp, vp]
+    lib.inkattn_sconv_paged.restype = i32
     lib.inkattn_relattn_prefill.argtypes = [dp, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp,
                                             vp, vp, vp, vp]
     lib.inkattn_relattn_prefill.restype = i32
@@ -201,3 +205,15 @@ def inkattn_relattn_decode_mq(desc, num_seqs, num_tokens, max_q_len, max_seq_len
                                         _ptr(out), _ptr(lse), num_splits, _ptr(workspace),
                                         workspace_bytes, _stream(stream))
     _check(st, "inkattn_relattn_decode_mq")
+
+
+def inkattn_sconv_paged(dtype, num_kv_heads, head_dim, num_seqs, num_tokens, max_chunk_len,
+                        k_in, v_in, conv_w, cu_seqlens, seq_lens, state_block_table, k_state,
+                        v_state, slot_mapping, k_cache, v_cache, stream=None):
+    st = _lib.inkattn_sconv_paged(dtype, num_kv_heads, head_dim, num_seqs, num_tokens,
+                                  max_chunk_len, _ptr(k_in), _ptr(v_in), _ptr(conv_w),
+                                  _ptr(cu_seqlens), _ptr(seq_lens), _ptr(state_block_table),
+                                  state_block_table.shape[1], _ptr(k_state), _ptr(v_state),
+                                  _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+                                  _stream(stream))
+    _check(st, "inkattn_sconv_paged")

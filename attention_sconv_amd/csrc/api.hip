@@ -113,6 +113,34 @@ inkattn_status_t inkattn_sconv(int32_t dtype, int32_t num_kv_heads, int32_t head
                                         (hipStream_t)stream));
 }
 
+inkattn_status_t inkattn_sconv_paged(int32_t dtype, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t num_seqs, int32_t num_tokens,
+                                     int32_t max_chunk_len, const void* k_in, const void* v_in,
+                                     const void* conv_w, const int32_t* cu_seqlens,
+                                     const int32_t* seq_lens, const int32_t* state_block_table,
+                                     int32_t max_state_blocks, void* k_state, void* v_state,
+                                     const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                     void* stream) {
+  if (dtype != INKATTN_FP32 && dtype != INKATTN_BF16) return INKATTN_ENOTSUP;
+  if (head_dim != 128) return INKATTN_ENOTSUP;
+  if (num_kv_heads < 1) return INKATTN_EINVAL;
+  if (num_kv_heads > 64) return INKATTN_ENOTSUP;       // one thread per 8 channels, <= 1024
+  if (num_seqs < 0 || num_tokens < 0 || max_chunk_len < 0) return INKATTN_EINVAL;
+  if (num_seqs == 0 || num_tokens == 0 || max_chunk_len == 0) return INKATTN_OK;
+  if (max_state_blocks < 1) return INKATTN_EINVAL;
+  if (!k_in || !v_in || !conv_w || !cu_seqlens || !seq_lens || !state_block_table || !k_state ||
+      !v_state || !slot_mapping || !k_cache || !v_cache)
+    return INKATTN_EINVAL;
+  if (!aligned16(k_in) || !aligned16(v_in) || !aligned16(conv_w) || !aligned16(k_state) ||
+      !aligned16(v_state) || !aligned16(k_cache) || !aligned16(v_cache))
+    return INKATTN_EINVAL;
+  return from_hip(inkattn::launch_sconv_paged(dtype, num_kv_heads, num_seqs, max_chunk_len,
+                                              k_in, v_in, conv_w, cu_seqlens, seq_lens,
+                                              state_block_table, max_state_blocks, k_state,
+                                              v_state, slot_mapping, k_cache, v_cache,
+                                              (hipStream_t)stream));
+}
+
 inkattn_status_t inkattn_relattn_prefill(const inkattn_attn_desc_t* desc, int32_t num_seqs,
                                          int32_t num_tokens, int32_t max_q_len,
                                          const void* q, const void* k_cache,

@@ -17,6 +17,13 @@ hipError_t launch_sconv(int dtype, int Hkv, int num_seqs, int max_chunk_len,
                         const int32_t* cu_seqlens, const int32_t* slot_mapping,
                         void* k_cache, void* v_cache, hipStream_t stream);
 
+hipError_t launch_sconv_paged(int dtype, int Hkv, int num_seqs, int max_chunk_len,
+                              const void* k_in, const void* v_in, const void* conv_w,
+                              const int32_t* cu_seqlens, const int32_t* seq_lens,
+                              const int32_t* state_block_table, int max_state_blocks,
+                              void* k_state, void* v_state, const int32_t* slot_mapping,
+                              void* k_cache, void* v_cache, hipStream_t stream);
+
 struct AttnShape {
   int dtype, Hq, Hkv, window, bias_len;
 };

@@ -17,6 +17,15 @@
 // state, so the in-place state update is race-free.
 // Memory-bound: every input byte is read once (plus a 3-row halo per chunk)
 // and every output byte written once.
+//
+// Paged state (kPaged): the pre-convolution rows of every token are kept in a
+// paged cache of their own, [block][128 tokens][Hkv*128 channels], addressed
+// through a block table like the K/V cache: the sconv cache as the K/V cache
+// of a virtual sliding-window layer of window 3 (vLLM Integration &
+// Optimization / Managing the sconv cache: blocks older than the window can
+// be evicted, and prefix caching covers the sconv state too).  A chunk at
+// positions ctx .. ctx+n-1 reads its halo ctx-3 .. ctx-1 from there (zero
+// before position 0) and writes its own rows there.
 #include "device_common.h"
 #include "launch.h"
 
@@ -25,13 +34,22 @@ namespace inkattn {
 constexpr int kSconvTok = 8;          // tokens per thread
 constexpr int kSconvRows = 4;         // token chunks per work-group (blockDim.y)
 
-template <typename T>
+// Paged-state arguments (unused by the dense-state kernel).
+struct SconvPaged {
+  const int32_t* seq_lens;        // chunk of sequence b ends at position seq_lens[b]-1
+  const int32_t* block_table;     // [num_seqs][max_blocks] blocks of the state cache
+  int max_blocks;
+  void* k_state;                  // [blocks][128][C] pre-convolution keys
+  void* v_state;                  // [blocks][128][C] pre-convolution values
+};
+
+template <typename T, bool kPaged>
 __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
     int C, int Hkv, const T* __restrict__ k_in, const T* __restrict__ v_in,
     const T* __restrict__ conv_w, T* __restrict__ conv_state,
     const int32_t* __restrict__ state_slot, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ slot_mapping, T* __restrict__ k_cache,
-    T* __restrict__ v_cache) {
+    T* __restrict__ v_cache, SconvPaged pg) {
   const int which = blockIdx.z;              // 0 = keys, 1 = values
   const int b = blockIdx.y;
   const int r0 = (blockIdx.x * blockDim.y + threadIdx.y) * kSconvTok;   // first token (relative)
@@ -42,16 +60,28 @@ __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
 
   const T* x = (which ? v_in : k_in) + (size_t)t_begin * C + c0;
   const T* wp = conv_w + ((size_t)which * C + c0) * 4;
-  T* st = conv_state + ((size_t)state_slot[b] * 2 + which) * 3 * C + c0;
+  T* st = kPaged ? nullptr : conv_state + ((size_t)state_slot[b] * 2 + which) * 3 * C + c0;
+  // Paged state: position of the chunk's first token, and the slot of a
+  // position in the state cache.
+  const int ctx = kPaged ? pg.seq_lens[b] - n : 0;
+  T* pst = kPaged ? static_cast<T*>(which ? pg.v_state : pg.k_state) + c0 : nullptr;
+  auto state_row = [&](int p) {
+    const int32_t blk = pg.block_table[(size_t)b * pg.max_blocks + (p >> 7)];
+    return pst + ((size_t)blk * kPage + (p & (kPage - 1))) * C;
+  };
 
   // All inputs of the chunk and its 3-token halo are loaded up front (the
-  // halo before the sequence start comes from the cached state).
+  // halo before the chunk comes from the cached state).
   Frag8<T> xs[kSconvTok + 3];
 #pragma unroll
   for (int k = 0; k < kSconvTok + 3; ++k) {
     const int rel = r0 - 3 + k;
-    xs[k] = rel < 0 ? Frag8<T>::load(st + (size_t)(rel + 3) * C)
-                    : (rel < n ? Frag8<T>::load(x + (size_t)rel * C) : Frag8<T>::zero());
+    if (rel >= 0)
+      xs[k] = rel < n ? Frag8<T>::load(x + (size_t)rel * C) : Frag8<T>::zero();
+    else if (!kPaged)
+      xs[k] = Frag8<T>::load(st + (size_t)(rel + 3) * C);
+    else
+      xs[k] = ctx + rel >= 0 ? Frag8<T>::load(state_row(ctx + rel)) : Frag8<T>::zero();
   }
   int slot[kSconvTok];
 #pragma unroll
@@ -117,7 +147,14 @@ __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
     }
   }
 
-  if (r0 == 0) {
+  if constexpr (kPaged) {
+    // This thread's tokens' inputs go to the state cache (rows the halo
+    // reads of this call are all before the chunk, so nothing read here is
+    // written here).
+#pragma unroll
+    for (int t = 0; t < kSconvTok; ++t)
+      if (r0 + t < n) xs[t + 3].store(state_row(ctx + r0 + t));
+  } else if (r0 == 0) {
     // New state = last three rows of [old state; sequence inputs].  Only the
     // thread that owns the first chunk touches the state.
     Frag8<T> ns[3];
@@ -132,11 +169,13 @@ __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
   }
 }
 
-hipError_t launch_sconv(int dtype, int Hkv, int num_seqs, int max_chunk_len,
-                        const void* k_in, const void* v_in, const void* conv_w,
-                        void* conv_state, const int32_t* state_slot,
-                        const int32_t* cu_seqlens, const int32_t* slot_mapping,
-                        void* k_cache, void* v_cache, hipStream_t stream) {
+template <bool kPaged>
+hipError_t launch_sconv_any(int dtype, int Hkv, int num_seqs, int max_chunk_len,
+                            const void* k_in, const void* v_in, const void* conv_w,
+                            void* conv_state, const int32_t* state_slot,
+                            const int32_t* cu_seqlens, const int32_t* slot_mapping,
+                            void* k_cache, void* v_cache, const SconvPaged& pg,
+                            hipStream_t stream) {
   const int C = Hkv * kHeadDim;
   const int per_block = kSconvTok * kSconvRows;
   dim3 grid((max_chunk_len + per_block - 1) / per_block, num_seqs, 2);
@@ -146,17 +185,41 @@ hipError_t launch_sconv(int dtype, int Hkv, int num_seqs, int max_chunk_len,
     grid.x = (max_chunk_len + kSconvTok * block.y - 1) / (kSconvTok * block.y);
   }
   if (dtype == kDtypeBf16) {
-    hipLaunchKernelGGL(sconv_cache_write_kernel<bf16>, grid, block, 0, stream, C, Hkv,
+    hipLaunchKernelGGL((sconv_cache_write_kernel<bf16, kPaged>), grid, block, 0, stream, C, Hkv,
                        (const bf16*)k_in, (const bf16*)v_in, (const bf16*)conv_w,
                        (bf16*)conv_state, state_slot, cu_seqlens, slot_mapping,
-                       (bf16*)k_cache, (bf16*)v_cache);
+                       (bf16*)k_cache, (bf16*)v_cache, pg);
   } else {
-    hipLaunchKernelGGL(sconv_cache_write_kernel<float>, grid, block, 0, stream, C, Hkv,
+    hipLaunchKernelGGL((sconv_cache_write_kernel<float, kPaged>), grid, block, 0, stream, C, Hkv,
                        (const float*)k_in, (const float*)v_in, (const float*)conv_w,
                        (float*)conv_state, state_slot, cu_seqlens, slot_mapping,
-                       (float*)k_cache, (float*)v_cache);
+                       (float*)k_cache, (float*)v_cache, pg);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_sconv(int dtype, int Hkv, int num_seqs, int max_chunk_len,
+                        const void* k_in, const void* v_in, const void* conv_w,
+                        void* conv_state, const int32_t* state_slot,
+                        const int32_t* cu_seqlens, const int32_t* slot_mapping,
+                        void* k_cache, void* v_cache, hipStream_t stream) {
+  return launch_sconv_any<false>(dtype, Hkv, num_seqs, max_chunk_len, k_in, v_in, conv_w,
+                                 conv_state, state_slot, cu_seqlens, slot_mapping, k_cache,
+                                 v_cache, SconvPaged{nullptr, nullptr, 0, nullptr, nullptr},
+                                 stream);
+}
+
+hipError_t launch_sconv_paged(int dtype, int Hkv, int num_seqs, int max_chunk_len,
+                              const void* k_in, const void* v_in, const void* conv_w,
+                              const int32_t* cu_seqlens, const int32_t* seq_lens,
+                              const int32_t* state_block_table, int max_state_blocks,
+                              void* k_state, void* v_state, const int32_t* slot_mapping,
+                              void* k_cache, void* v_cache, hipStream_t stream) {
+  return launch_sconv_any<true>(dtype, Hkv, num_seqs, max_chunk_len, k_in, v_in, conv_w,
+                                nullptr, nullptr, cu_seqlens, slot_mapping, k_cache, v_cache,
+                                SconvPaged{seq_lens, state_block_table, max_state_blocks,
+                                           k_state, v_state},
+                                stream);
 }
 
 }  // namespace inkattn

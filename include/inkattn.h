@@ -102,6 +102,33 @@ inkattn_status_t inkattn_sconv(int32_t dtype, int32_t num_kv_heads, int32_t head
                                const int32_t* cu_seqlens, const int32_t* slot_mapping,
                                void* k_cache, void* v_cache, void* stream);
 
+/* The same short convolution with the sconv state kept in a paged cache of
+ * its own, as the K/V cache of a virtual sliding-window layer of window 3
+ * ([A] Managing the sconv cache: blocks outside the window can be evicted,
+ * and prefix caching covers the sconv state too).  Instead of a per-sequence
+ * state slot, every token's pre-convolution key and value rows are kept:
+ *   k_state, v_state  [num_state_blocks][128 tokens][Hkv*128]
+ * Position p of sequence b is row p % 128 of block
+ * state_block_table[b][p / 128].  Sequence b's chunk (tokens cu_seqlens[b] ..
+ * cu_seqlens[b+1]-1, n of them) sits at positions seq_lens[b]-n ..
+ * seq_lens[b]-1; its convolution reads positions seq_lens[b]-n-3 ..
+ * seq_lens[b]-n-1 from the state cache (zero before position 0), then writes
+ * the chunk's own input rows there.  The outputs go to k_cache/v_cache at
+ * slot_mapping[t] exactly as inkattn_sconv writes them.  Sequences may share
+ * state blocks of their common prefix (read only); the blocks a call writes
+ * must not be read by another sequence in the same call.
+ *   state_block_table int32 [num_seqs][max_state_blocks]
+ * num_tokens == 0 or num_seqs == 0 is a no-op returning INKATTN_OK; other
+ * errors as inkattn_sconv. */
+inkattn_status_t inkattn_sconv_paged(int32_t dtype, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t num_seqs, int32_t num_tokens,
+                                     int32_t max_chunk_len, const void* k_in, const void* v_in,
+                                     const void* conv_w, const int32_t* cu_seqlens,
+                                     const int32_t* seq_lens, const int32_t* state_block_table,
+                                     int32_t max_state_blocks, void* k_state, void* v_state,
+                                     const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                     void* stream);
+
 /* Relative-position GQA attention over a chunk of new tokens per sequence
  * ([A] Attention; [A] FA4 with sheared bias):
  *   logit[h,i,j] = q_i . k_j / sqrt(128) + bias[h][min(i-j, R-1)]

@@ -209,3 +209,24 @@ def test_decode_mq_splits_and_workspace():
     rows = 10 * 32 * 3
     assert n == rows * 128 * 4 + ((rows * 4 + 15) // 16) * 16
     assert ink.inkattn_relattn_decode_mq_workspace_size(d, 2, 10, 17, 16384, 3) == 0
+
+
+def _sconv_paged(**kw):
+    args = dict(dtype=ink.BF16, Hkv=4, d=128, seqs=2, toks=10, maxlen=8, k=FAKE, v=FAKE,
+                w=FAKE, cu=FAKE, sl=FAKE, sbt=FAKE, msb=4, ks=FAKE, vs=FAKE, slot=FAKE,
+                kc=FAKE, vc=FAKE)
+    args.update(kw)
+    return ink._lib._lib.inkattn_sconv_paged(
+        args["dtype"], args["Hkv"], args["d"], args["seqs"], args["toks"], args["maxlen"],
+        args["k"], args["v"], args["w"], args["cu"], args["sl"], args["sbt"], args["msb"],
+        args["ks"], args["vs"], args["slot"], args["kc"], args["vc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), 2), (dict(d=64), 2), (dict(Hkv=0), 1), (dict(Hkv=65), 2),
+    (dict(seqs=-1), 1), (dict(seqs=0), 0), (dict(toks=0), 0), (dict(msb=0), 1),
+    (dict(sl=None), 1), (dict(sbt=None), 1), (dict(ks=None), 1), (dict(vs=None), 1),
+    (dict(ks=FAKE + 8), 1), (dict(kc=None), 1),
+])
+def test_sconv_paged_host_validation(kw, status):
+    assert _sconv_paged(**kw) == status
