@@ -5,6 +5,8 @@
                                  three-token state update;
 * ``inkattn_sconv_paged``      -- the same with the sconv state kept in a paged
                                  cache (a window-3 virtual layer; prefix caching);
+* ``inkattn_sconv_out``        -- the same convolution on a plain activation
+                                 tensor (attention output, MoE output);
 * ``inkattn_relattn_prefill``  -- relative-position GQA attention over new
                                  tokens (bf16/fp32 MFMA, sheared bias band);
 * ``inkattn_relattn_decode``   -- split-K paged decode plus log-sum-exp merge;
@@ -24,7 +26,7 @@ from ._lib import (  # noqa: F401
     AttnDesc, InkattnError, make_desc, status_string,
     inkattn_sconv, inkattn_relattn_prefill, inkattn_relattn_decode,
     inkattn_relattn_decode_num_splits, inkattn_relattn_decode_workspace_size,
-    inkattn_sconv_paged,
+    inkattn_sconv_paged, inkattn_sconv_out,
     inkattn_relattn_decode_mq, inkattn_relattn_decode_mq_num_splits,
     inkattn_relattn_decode_mq_workspace_size,
     inkattn_probe_mfma_bf16, inkattn_probe_stream_read,

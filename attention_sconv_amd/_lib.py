@@ -20,6 +20,7 @@ FP32, BF16 = 0, 1
 EXPORTED = (
     "inkattn_sconv",
     "inkattn_sconv_paged",
+    "inkattn_sconv_out",
     "inkattn_relattn_prefill",
     "inkattn_relattn_decode_num_splits",
     "inkattn_relattn_decode_workspace_size",
@@ -66,6 +67,8 @@ def _load():
     lib.inkattn_sconv_paged.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                         i32, vp, vp, vp, vp, vp, vp]
     lib.inkattn_sconv_paged.restype = i32
+    lib.inkattn_sconv_out.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.inkattn_sconv_out.restype = i32
     lib.inkattn_relattn_prefill.argtypes = [dp, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp,
                                             vp, vp, vp, vp]
     lib.inkattn_relattn_prefill.restype = i32
@@ -217,3 +220,11 @@ def inkattn_sconv_paged(dtype, num_kv_heads, head_dim, num_seqs, num_tokens, max
                                   _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
                                   _stream(stream))
     _check(st, "inkattn_sconv_paged")
+
+
+def inkattn_sconv_out(dtype, channels, num_seqs, num_tokens, max_chunk_len, x, conv_w,
+                      conv_state, state_slot, cu_seqlens, y, stream=None):
+    st = _lib.inkattn_sconv_out(dtype, channels, num_seqs, num_tokens, max_chunk_len, _ptr(x),
+                                _ptr(conv_w), _ptr(conv_state), _ptr(state_slot),
+                                _ptr(cu_seqlens), _ptr(y), _stream(stream))
+    _check(st, "inkattn_sconv_out")

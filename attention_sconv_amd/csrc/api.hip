@@ -141,6 +141,30 @@ inkattn_status_t inkattn_sconv_paged(int32_t dtype, int32_t num_kv_heads, int32_
                                               (hipStream_t)stream));
 }
 
+inkattn_status_t inkattn_sconv_out(int32_t dtype, int32_t channels, int32_t num_seqs,
+                                   int32_t num_tokens, int32_t max_chunk_len, const void* x,
+                                   const void* conv_w, void* conv_state,
+                                   const int32_t* state_slot, const int32_t* cu_seqlens, void* y,
+                                   void* stream) {
+  if (dtype != INKATTN_FP32 && dtype != INKATTN_BF16) return INKATTN_ENOTSUP;
+  if (channels < 8 || channels % 8 != 0) return INKATTN_EINVAL;
+  if (channels > 8192) return INKATTN_ENOTSUP;          // one thread per 8 channels, <= 1024
+  if (num_seqs < 0 || num_tokens < 0 || max_chunk_len < 0) return INKATTN_EINVAL;
+  if (num_seqs == 0 || num_tokens == 0 || max_chunk_len == 0) return INKATTN_OK;
+  if (!x || !conv_w || !conv_state || !state_slot || !cu_seqlens || !y) return INKATTN_EINVAL;
+  if (!aligned16(x) || !aligned16(conv_w) || !aligned16(conv_state) || !aligned16(y))
+    return INKATTN_EINVAL;
+  {
+    // threads read halo rows of x that other threads would overwrite in y
+    const size_t bytes = (size_t)num_tokens * channels * (dtype == INKATTN_BF16 ? 2 : 4);
+    const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
+    if (xb < yb + bytes && yb < xb + bytes) return INKATTN_EINVAL;
+  }
+  return from_hip(inkattn::launch_sconv_out(dtype, channels, num_seqs, max_chunk_len, x,
+                                            conv_w, conv_state, state_slot, cu_seqlens, y,
+                                            (hipStream_t)stream));
+}
+
 inkattn_status_t inkattn_relattn_prefill(const inkattn_attn_desc_t* desc, int32_t num_seqs,
                                          int32_t num_tokens, int32_t max_q_len,
                                          const void* q, const void* k_cache,

@@ -24,6 +24,10 @@ hipError_t launch_sconv_paged(int dtype, int Hkv, int num_seqs, int max_chunk_le
                               void* k_state, void* v_state, const int32_t* slot_mapping,
                               void* k_cache, void* v_cache, hipStream_t stream);
 
+hipError_t launch_sconv_out(int dtype, int C, int num_seqs, int max_chunk_len, const void* x,
+                            const void* conv_w, void* conv_state, const int32_t* state_slot,
+                            const int32_t* cu_seqlens, void* y, hipStream_t stream);
+
 struct AttnShape {
   int dtype, Hq, Hkv, window, bias_len;
 };

@@ -169,6 +169,86 @@ __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
   }
 }
 
+// Short convolution of a plain activation tensor [tokens][C] (the attention
+// output or the MoE output: Model Architecture / Sconv names four sconv
+// modules per layer, on keys, values, attention output and MoE output), with
+// the dense three-token state [slots][3][C].  Same work split as above: each
+// thread owns 8 channels and kSconvTok tokens of one sequence.
+template <typename T>
+__global__ __launch_bounds__(1024) void sconv_out_kernel(
+    int C, const T* __restrict__ x_in, const T* __restrict__ conv_w, T* __restrict__ conv_state,
+    const int32_t* __restrict__ state_slot, const int32_t* __restrict__ cu_seqlens,
+    T* __restrict__ y_out) {
+  const int b = blockIdx.y;
+  const int r0 = (blockIdx.x * blockDim.y + threadIdx.y) * kSconvTok;   // first token (relative)
+  const int c0 = threadIdx.x * 8;
+  const int t_begin = cu_seqlens[b];
+  const int n = cu_seqlens[b + 1] - t_begin;
+  if (r0 >= n) return;
+  const T* x = x_in + (size_t)t_begin * C + c0;
+  T* y = y_out + (size_t)t_begin * C + c0;
+  T* st = conv_state + (size_t)state_slot[b] * 3 * C + c0;
+
+  Frag8<T> xs[kSconvTok + 3];
+#pragma unroll
+  for (int k = 0; k < kSconvTok + 3; ++k) {
+    const int rel = r0 - 3 + k;
+    xs[k] = rel < 0 ? Frag8<T>::load(st + (size_t)(rel + 3) * C)
+                    : (rel < n ? Frag8<T>::load(x + (size_t)rel * C) : Frag8<T>::zero());
+  }
+  float w[8][4];
+  {
+    const T* wp = conv_w + (size_t)c0 * 4;
+    const Frag8<T> f0 = Frag8<T>::load(wp), f1 = Frag8<T>::load(wp + 8),
+                   f2 = Frag8<T>::load(wp + 16), f3 = Frag8<T>::load(wp + 24);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const Frag8<T>& f = e < 2 ? f0 : e < 4 ? f1 : e < 6 ? f2 : f3;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[e][k] = f.get((e & 1) * 4 + k);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kSconvTok; ++t) {
+    if (r0 + t >= n) break;
+    float yt[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      yt[e] = w[e][0] * xs[t].get(e) + w[e][1] * xs[t + 1].get(e) +
+              w[e][2] * xs[t + 2].get(e) + w[e][3] * xs[t + 3].get(e);
+    Frag8<T>::pack(yt).store(y + (size_t)(r0 + t) * C);
+  }
+  if (r0 == 0) {
+    // New state = last three rows of [old state; inputs]; only the thread
+    // that owns the first chunk touches the state.
+    Frag8<T> ns[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int rel = n - 3 + k;
+      ns[k] = rel >= 0 ? Frag8<T>::load(x + (size_t)rel * C)
+                       : Frag8<T>::load(st + (size_t)(rel + 3) * C);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) ns[k].store(st + (size_t)k * C);
+  }
+}
+
+hipError_t launch_sconv_out(int dtype, int C, int num_seqs, int max_chunk_len, const void* x,
+                            const void* conv_w, void* conv_state, const int32_t* state_slot,
+                            const int32_t* cu_seqlens, void* y, hipStream_t stream) {
+  dim3 block(C / 8, 1);
+  block.y = (unsigned)max(1, min(kSconvRows, 1024 / (C / 8)));
+  dim3 grid((max_chunk_len + kSconvTok * block.y - 1) / (kSconvTok * block.y), num_seqs, 1);
+  if (dtype == kDtypeBf16)
+    hipLaunchKernelGGL(sconv_out_kernel<bf16>, grid, block, 0, stream, C, (const bf16*)x,
+                       (const bf16*)conv_w, (bf16*)conv_state, state_slot, cu_seqlens, (bf16*)y);
+  else
+    hipLaunchKernelGGL(sconv_out_kernel<float>, grid, block, 0, stream, C, (const float*)x,
+                       (const float*)conv_w, (float*)conv_state, state_slot, cu_seqlens,
+                       (float*)y);
+  return hipGetLastError();
+}
+
 template <bool kPaged>
 hipError_t launch_sconv_any(int dtype, int Hkv, int num_seqs, int max_chunk_len,
                             const void* k_in, const void* v_in, const void* conv_w,

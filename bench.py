@@ -268,6 +268,8 @@ def main():
     ap.add_argument("--no-mtp", action="store_true",
                     help="skip the MTP-verification decode leg (it launches the decode kernel "
                          "with another shape)")
+    ap.add_argument("--no-sconv-out", action="store_true",
+                    help="skip the leg that times the sconv of a plain activation tensor")
     ap.add_argument("--steady-s", type=float, default=0.3,
                     help="seconds of untimed back-to-back steps before the warmup steps, "
                          "so that the timed steps run at the sustained shader clock")
@@ -429,6 +431,44 @@ def main():
         del md
 
     import attention_sconv_amd as ink
+    # ---------------- sconv of a plain activation (attention / MoE output)
+    if not args.no_sconv_out:
+        sc = synth.make_sconv_out_case("bf16", [8192] * 4, 4096, seed=0, extra_slots=0)
+        td = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(
+            torch.bfloat16)
+        sx, sw, sst = td(sc.x), td(sc.conv_w), td(sc.conv_state)
+        sslot = torch.from_numpy(sc.state_slot).cuda()
+        scu = torch.from_numpy(sc.cu_seqlens.astype(np.int32)).cuda()
+        sy = torch.empty_like(sx)
+        s_bytes = 2 * sx.numel() * 2 + 2 * sst.numel() * 2 + sw.numel() * 2
+
+        def sstep(ev):
+            if ev is not None:
+                ev[0].record()
+            ink.inkattn_sconv_out(ink.BF16, 4096, 4, sx.shape[0], 8192, sx, sw, sst, sslot,
+                                  scu, sy)
+            if ev is not None:
+                ev[1].record()
+
+        print("[bench] sconv_out", file=sys.stderr, flush=True)
+        steady_clocks(torch, sstep, 0.1)
+        _, sks = time_region(torch, sstep, None, max(args.steps, 20), args.warmup)
+        s_ms = float(np.median(sks))
+        s_gbs = s_bytes / (s_ms * 1e-3) / 1e9
+        result["sconv_out"] = {
+            "workload": "4 x 8192 tokens x 4096 channels, bf16 (a stand-in width)",
+            "ms_median": round(s_ms, 4), "ms_min": round(min(sks), 4), "bytes": s_bytes,
+            "achieved": round(s_gbs, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
+            "frac": round(s_gbs / PEAK_HBM_GBS, 4),
+            "traffic": recorded_traffic(
+                "sconv_out_bf16_4x8192x4096.traffic.txt",
+                ["attention_sconv_amd/csrc/sconv.hip",
+                 "attention_sconv_amd/csrc/device_common.h"]),
+            "note": "inkattn_sconv_out; bytes = x read + y written + state read and written "
+                    "+ taps",
+        }
+        del sx, sy, sst
+
     print("[bench] measured ceilings", file=sys.stderr, flush=True)
     ceil = ceilings(torch, ink)
     result["ceilings"] = ceil

@@ -129,6 +129,29 @@ inkattn_status_t inkattn_sconv_paged(int32_t dtype, int32_t num_kv_heads, int32_
                                      const int32_t* slot_mapping, void* k_cache, void* v_cache,
                                      void* stream);
 
+/* Short convolution of a plain activation tensor: the attention output and
+ * the MoE output each pass through a sconv of their own ([A] Model
+ * Architecture / Sconv: four per layer, on keys, values, attention output and
+ * MoE output), with the same taps and three-token state as inkattn_sconv but
+ * no KV-cache write:
+ *   y[t][c] = sum_{k=0..3} conv_w[c][k] * xp[t+k][c],  xp = [state; chunk]
+ * and the state becomes the last three rows of xp.
+ *   x, y        [num_tokens][channels]  sequences packed back to back; y must
+ *                                       not overlap x
+ *   conv_w      [channels][4]           conv_w[c][3] weights the current token
+ *   conv_state  [num_slots][3][channels] read, then updated in place
+ *   state_slot  int32 [num_seqs]        distinct within one call
+ *   cu_seqlens  int32 [num_seqs+1]
+ *   max_chunk_len: host upper bound of cu_seqlens[b+1]-cu_seqlens[b].
+ * channels: a multiple of 8 (EINVAL otherwise), at most 8192 (ENOTSUP).
+ * Pointers 16-byte aligned.  num_tokens == 0 or num_seqs == 0 is a no-op
+ * returning INKATTN_OK. */
+inkattn_status_t inkattn_sconv_out(int32_t dtype, int32_t channels, int32_t num_seqs,
+                                   int32_t num_tokens, int32_t max_chunk_len, const void* x,
+                                   const void* conv_w, void* conv_state,
+                                   const int32_t* state_slot, const int32_t* cu_seqlens, void* y,
+                                   void* stream);
+
 /* Relative-position GQA attention over a chunk of new tokens per sequence
  * ([A] Attention; [A] FA4 with sheared bias):
  *   logit[h,i,j] = q_i . k_j / sqrt(128) + bias[h][min(i-j, R-1)]

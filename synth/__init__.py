@@ -209,3 +209,37 @@ def workload_case(wl: Workload, seed=0, past_device=None, batch=None):
     return make_case(wl.dtype, [wl.q_len] * B, [wl.seq_len - wl.q_len] * B, wl.num_q_heads,
                      wl.num_kv_heads, wl.window, wl.bias_len, seed=seed,
                      past_device=past_device)
+
+
+@dataclass
+class SconvOutCase:
+    """Inputs of the short convolution on a plain activation tensor."""
+    dtype: str
+    x: np.ndarray            # [N, C]
+    conv_w: np.ndarray       # [C, 4]
+    conv_state: np.ndarray   # [num_slots, 3, C]
+    state_slot: np.ndarray   # [B] int32, distinct
+    cu_seqlens: np.ndarray   # [B + 1] int64
+    q_lens: np.ndarray       # [B]
+
+
+def make_sconv_out_case(dtype, q_lens, channels, seed=0, extra_slots=2, fresh=None):
+    """Ragged chunks of a [tokens][channels] activation, per-channel taps and a
+    state table with ``extra_slots`` rows no sequence owns.  ``fresh[b]`` (all
+    False by default) gives sequence b a zero state."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    B = len(q_lens)
+    cu = np.zeros(B + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(q_lens)
+    x = _draw(rng, (int(cu[-1]), channels), 1.0, dtype)
+    w = _draw(rng, (channels, 4), 0.5, dtype)
+    slots = B + int(extra_slots)
+    state = _draw(rng, (slots, 3, channels), 1.0, dtype)
+    state_slot = rng.permutation(slots)[:B].astype(np.int32)
+    if fresh is not None:
+        for b in range(B):
+            if fresh[b]:
+                state[state_slot[b]] = 0.0
+    return SconvOutCase(dtype=dtype, x=x, conv_w=w, conv_state=state, state_slot=state_slot,
+                        cu_seqlens=cu, q_lens=q_lens)

@@ -230,3 +230,25 @@ def _sconv_paged(**kw):
 ])
 def test_sconv_paged_host_validation(kw, status):
     assert _sconv_paged(**kw) == status
+
+
+def _sconv_out(**kw):
+    args = dict(dtype=ink.BF16, C=1024, seqs=2, toks=10, maxlen=8, x=FAKE, w=FAKE, st=FAKE,
+                slot=FAKE, cu=FAKE, y=FAKE + (1 << 20))
+    args.update(kw)
+    return ink._lib._lib.inkattn_sconv_out(
+        args["dtype"], args["C"], args["seqs"], args["toks"], args["maxlen"], args["x"],
+        args["w"], args["st"], args["slot"], args["cu"], args["y"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), 2), (dict(C=0), 1), (dict(C=12), 1), (dict(C=8200), 2),
+    (dict(seqs=-1), 1), (dict(seqs=0), 0), (dict(toks=0), 0), (dict(maxlen=0), 0),
+    (dict(x=None), 1), (dict(w=None), 1), (dict(st=None), 1), (dict(slot=None), 1),
+    (dict(cu=None), 1), (dict(y=None), 1), (dict(x=FAKE + 8), 1),
+    (dict(y=FAKE), 1),                                        # in place
+    (dict(y=FAKE + 10 * 1024 * 2 - 16), 1),                   # y starts inside x
+    (dict(x=FAKE + (1 << 20) + 16), 1),                       # x starts inside y
+])
+def test_sconv_out_host_validation(kw, status):
+    assert _sconv_out(**kw) == status
