@@ -29,13 +29,18 @@ pages this library is built from):
   (news article, *FA4 with sheared bias*, where the number of KV splits is
   chosen per configuration).
 
+* ``fp8``        -- the OCP E4M3 code of a scaled key or value and what a
+  cached code reads back as, for an FP8 KV cache (news article, *Roadmap*:
+  FP8 for the global-attention layers).  Attention over such a cache is the
+  attention above on the read-back keys and values.
+
 Everything is evaluated in float64 straight from the definitions: no tiling,
 no online softmax, no splits.  Inputs may be float32 or bfloat16-representable
 values held in float32; they are upcast exactly.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, library routines (torch float64 ``conv1d`` and
-``scaled_dot_product_attention`` on the CPU), metamorphic invariants and a
+``scaled_dot_product_attention`` on the CPU, torch's ``float8_e4m3fn``), metamorphic invariants and a
 pure-Python brute force.  No function is "parity unpinned".
 """
 
@@ -48,3 +53,4 @@ from .attention import (  # noqa: F401
     relattn_decode,
     lse_merge,
 )
+from . import fp8  # noqa: F401
