@@ -7,6 +7,9 @@
                                  cache (a window-3 virtual layer; prefix caching);
 * ``inkattn_sconv_out``        -- the same convolution on a plain activation
                                  tensor (attention output, MoE output);
+* ``inkattn_sconv_fp8``, ``inkattn_relattn_decode_fp8`` -- the sconv cache
+                                 write and the (multi-query) decode with an
+                                 FP8 (OCP E4M3, scaled) KV cache;
 * ``inkattn_relattn_prefill``  -- relative-position GQA attention over new
                                  tokens (bf16/fp32 MFMA, sheared bias band);
 * ``inkattn_relattn_decode``   -- split-K paged decode plus log-sum-exp merge;
@@ -26,7 +29,7 @@ from ._lib import (  # noqa: F401
     AttnDesc, InkattnError, make_desc, status_string,
     inkattn_sconv, inkattn_relattn_prefill, inkattn_relattn_decode,
     inkattn_relattn_decode_num_splits, inkattn_relattn_decode_workspace_size,
-    inkattn_sconv_paged, inkattn_sconv_out,
+    inkattn_sconv_paged, inkattn_sconv_out, inkattn_sconv_fp8, inkattn_relattn_decode_fp8,
     inkattn_relattn_decode_mq, inkattn_relattn_decode_mq_num_splits,
     inkattn_relattn_decode_mq_workspace_size,
     inkattn_probe_mfma_bf16, inkattn_probe_stream_read,

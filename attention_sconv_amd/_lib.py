@@ -21,6 +21,8 @@ EXPORTED = (
     "inkattn_sconv",
     "inkattn_sconv_paged",
     "inkattn_sconv_out",
+    "inkattn_sconv_fp8",
+    "inkattn_relattn_decode_fp8",
     "inkattn_relattn_prefill",
     "inkattn_relattn_decode_num_splits",
     "inkattn_relattn_decode_workspace_size",
@@ -69,6 +71,13 @@ def _load():
     lib.inkattn_sconv_paged.restype = i32
     lib.inkattn_sconv_out.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.inkattn_sconv_out.restype = i32
+    f32 = ctypes.c_float
+    lib.inkattn_sconv_fp8.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                      f32, f32, vp, vp, vp]
+    lib.inkattn_sconv_fp8.restype = i32
+    lib.inkattn_relattn_decode_fp8.argtypes = [dp, i32, i32, i32, i32, vp, vp, vp, f32, f32, vp,
+                                               i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.inkattn_relattn_decode_fp8.restype = i32
     lib.inkattn_relattn_prefill.argtypes = [dp, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp,
                                             vp, vp, vp, vp]
     lib.inkattn_relattn_prefill.restype = i32
@@ -228,3 +237,28 @@ def inkattn_sconv_out(dtype, channels, num_seqs, num_tokens, max_chunk_len, x, c
                                 _ptr(conv_w), _ptr(conv_state), _ptr(state_slot),
                                 _ptr(cu_seqlens), _ptr(y), _stream(stream))
     _check(st, "inkattn_sconv_out")
+
+
+def inkattn_sconv_fp8(dtype, num_kv_heads, head_dim, num_seqs, num_tokens, max_chunk_len, k_in,
+                      v_in, conv_w, conv_state, state_slot, cu_seqlens, slot_mapping, k_scale,
+                      v_scale, k_cache, v_cache, stream=None):
+    st = _lib.inkattn_sconv_fp8(dtype, num_kv_heads, head_dim, num_seqs, num_tokens,
+                                max_chunk_len, _ptr(k_in), _ptr(v_in), _ptr(conv_w),
+                                _ptr(conv_state), _ptr(state_slot), _ptr(cu_seqlens),
+                                _ptr(slot_mapping), k_scale, v_scale, _ptr(k_cache),
+                                _ptr(v_cache), _stream(stream))
+    _check(st, "inkattn_sconv_fp8")
+
+
+def inkattn_relattn_decode_fp8(desc, num_seqs, num_tokens, max_q_len, max_seq_len, q, k_cache,
+                               v_cache, k_scale, v_scale, block_table, max_blocks_per_seq,
+                               cu_seqlens_q, seq_lens, bias, out, lse=None, num_splits=0,
+                               workspace=None, workspace_bytes=0, stream=None):
+    st = _lib.inkattn_relattn_decode_fp8(ctypes.byref(desc), num_seqs, num_tokens, max_q_len,
+                                         max_seq_len, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         k_scale, v_scale, _ptr(block_table),
+                                         max_blocks_per_seq, _ptr(cu_seqlens_q),
+                                         _ptr(seq_lens), _ptr(bias), _ptr(out), _ptr(lse),
+                                         num_splits, _ptr(workspace), workspace_bytes,
+                                         _stream(stream))
+    _check(st, "inkattn_relattn_decode_fp8")

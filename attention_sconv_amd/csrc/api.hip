@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "launch.h"
 
 using inkattn::AttnShape;
@@ -16,6 +18,8 @@ constexpr int kDecodeTargetGroups = kCUs;   // (seq, kv-head, split) work-groups
 constexpr int kMaxDecodeQueries = 16;       // query tokens per sequence in one decode call
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// A cache scale must be positive and finite, with a finite reciprocal.
+bool fp8_scale_ok(float s) { return s > 0.0f && std::isfinite(s) && std::isfinite(1.0f / s); }
 
 inkattn_status_t check_desc(const inkattn_attn_desc_t* d) {
   if (!d) return INKATTN_EINVAL;
@@ -89,17 +93,20 @@ const char* inkattn_status_string(int32_t status) {
   }
 }
 
-inkattn_status_t inkattn_sconv(int32_t dtype, int32_t num_kv_heads, int32_t head_dim,
-                               int32_t num_seqs, int32_t num_tokens, int32_t max_chunk_len,
-                               const void* k_in, const void* v_in, const void* conv_w,
-                               void* conv_state, const int32_t* state_slot,
-                               const int32_t* cu_seqlens, const int32_t* slot_mapping,
-                               void* k_cache, void* v_cache, void* stream) {
+static inkattn_status_t sconv_common(int32_t dtype, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t num_seqs, int32_t num_tokens,
+                                     int32_t max_chunk_len, const void* k_in, const void* v_in,
+                                     const void* conv_w, void* conv_state,
+                                     const int32_t* state_slot, const int32_t* cu_seqlens,
+                                     const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                     const float* fp8_scales, void* stream) {
   if (dtype != INKATTN_FP32 && dtype != INKATTN_BF16) return INKATTN_ENOTSUP;
   if (head_dim != 128) return INKATTN_ENOTSUP;
   if (num_kv_heads < 1) return INKATTN_EINVAL;
   if (num_kv_heads > 64) return INKATTN_ENOTSUP;       // one thread per 8 channels, <= 1024
   if (num_seqs < 0 || num_tokens < 0 || max_chunk_len < 0) return INKATTN_EINVAL;
+  if (fp8_scales != nullptr && !(fp8_scale_ok(fp8_scales[0]) && fp8_scale_ok(fp8_scales[1])))
+    return INKATTN_EINVAL;
   if (num_seqs == 0 || num_tokens == 0 || max_chunk_len == 0) return INKATTN_OK;
   if (!k_in || !v_in || !conv_w || !conv_state || !state_slot || !cu_seqlens ||
       !slot_mapping || !k_cache || !v_cache)
@@ -109,8 +116,32 @@ inkattn_status_t inkattn_sconv(int32_t dtype, int32_t num_kv_heads, int32_t head
     return INKATTN_EINVAL;
   return from_hip(inkattn::launch_sconv(dtype, num_kv_heads, num_seqs, max_chunk_len, k_in,
                                         v_in, conv_w, conv_state, state_slot, cu_seqlens,
-                                        slot_mapping, k_cache, v_cache,
+                                        slot_mapping, k_cache, v_cache, fp8_scales,
                                         (hipStream_t)stream));
+}
+
+inkattn_status_t inkattn_sconv(int32_t dtype, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t num_seqs, int32_t num_tokens, int32_t max_chunk_len,
+                               const void* k_in, const void* v_in, const void* conv_w,
+                               void* conv_state, const int32_t* state_slot,
+                               const int32_t* cu_seqlens, const int32_t* slot_mapping,
+                               void* k_cache, void* v_cache, void* stream) {
+  return sconv_common(dtype, num_kv_heads, head_dim, num_seqs, num_tokens, max_chunk_len, k_in,
+                      v_in, conv_w, conv_state, state_slot, cu_seqlens, slot_mapping, k_cache,
+                      v_cache, nullptr, stream);
+}
+
+inkattn_status_t inkattn_sconv_fp8(int32_t dtype, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_seqs, int32_t num_tokens, int32_t max_chunk_len,
+                                   const void* k_in, const void* v_in, const void* conv_w,
+                                   void* conv_state, const int32_t* state_slot,
+                                   const int32_t* cu_seqlens, const int32_t* slot_mapping,
+                                   float k_scale, float v_scale, void* k_cache, void* v_cache,
+                                   void* stream) {
+  const float scales[2] = {k_scale, v_scale};
+  return sconv_common(dtype, num_kv_heads, head_dim, num_seqs, num_tokens, max_chunk_len, k_in,
+                      v_in, conv_w, conv_state, state_slot, cu_seqlens, slot_mapping, k_cache,
+                      v_cache, scales, stream);
 }
 
 inkattn_status_t inkattn_sconv_paged(int32_t dtype, int32_t num_kv_heads, int32_t head_dim,
@@ -234,7 +265,7 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
   float* part_lse = part_o + rows * 128;
   return from_hip(inkattn::launch_decode(shape_of(desc), num_seqs, num_seqs, 1, s, q, k_cache,
                                          v_cache, block_table, max_blocks_per_seq, nullptr,
-                                         seq_lens, bias, out, lse, part_o, part_lse,
+                                         seq_lens, bias, out, lse, part_o, part_lse, nullptr,
                                          (hipStream_t)stream));
 }
 
@@ -259,18 +290,23 @@ size_t inkattn_relattn_decode_mq_workspace_size(const inkattn_attn_desc_t* desc,
   return rows * 128 * sizeof(float) + ((rows * sizeof(float) + 15) & ~(size_t)15);
 }
 
-inkattn_status_t inkattn_relattn_decode_mq(const inkattn_attn_desc_t* desc, int32_t num_seqs,
-                                           int32_t num_tokens, int32_t max_q_len,
-                                           int32_t max_seq_len, const void* q,
-                                           const void* k_cache, const void* v_cache,
-                                           const int32_t* block_table,
-                                           int32_t max_blocks_per_seq,
-                                           const int32_t* cu_seqlens_q, const int32_t* seq_lens,
-                                           const void* bias, void* out, float* lse,
-                                           int32_t num_splits, void* workspace,
-                                           size_t workspace_bytes, void* stream) {
+static inkattn_status_t decode_mq_common(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                         int32_t num_tokens, int32_t max_q_len,
+                                         int32_t max_seq_len, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         const int32_t* block_table,
+                                         int32_t max_blocks_per_seq,
+                                         const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                         const void* bias, void* out, float* lse,
+                                         int32_t num_splits, void* workspace,
+                                         size_t workspace_bytes, const float* fp8_scales,
+                                         void* stream) {
   inkattn_status_t st = check_desc(desc);
   if (st != INKATTN_OK) return st;
+  if (fp8_scales != nullptr) {
+    if (desc->dtype != INKATTN_BF16) return INKATTN_ENOTSUP;
+    if (!fp8_scale_ok(fp8_scales[0]) || !fp8_scale_ok(fp8_scales[1])) return INKATTN_EINVAL;
+  }
   if (num_seqs < 0 || num_tokens < 0 || max_seq_len < 0 || num_splits < 0 || max_q_len < 0)
     return INKATTN_EINVAL;
   if (num_seqs == 0 || num_tokens == 0) return INKATTN_OK;
@@ -296,7 +332,39 @@ inkattn_status_t inkattn_relattn_decode_mq(const inkattn_attn_desc_t* desc, int3
   return from_hip(inkattn::launch_decode(shape_of(desc), num_seqs, num_tokens, max_q_len, s, q,
                                          k_cache, v_cache, block_table, max_blocks_per_seq,
                                          cu_seqlens_q, seq_lens, bias, out, lse, part_o,
-                                         part_lse, (hipStream_t)stream));
+                                         part_lse, fp8_scales, (hipStream_t)stream));
+}
+
+inkattn_status_t inkattn_relattn_decode_mq(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                           int32_t num_tokens, int32_t max_q_len,
+                                           int32_t max_seq_len, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const int32_t* block_table,
+                                           int32_t max_blocks_per_seq,
+                                           const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                           const void* bias, void* out, float* lse,
+                                           int32_t num_splits, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  return decode_mq_common(desc, num_seqs, num_tokens, max_q_len, max_seq_len, q, k_cache,
+                          v_cache, block_table, max_blocks_per_seq, cu_seqlens_q, seq_lens, bias,
+                          out, lse, num_splits, workspace, workspace_bytes, nullptr, stream);
+}
+
+inkattn_status_t inkattn_relattn_decode_fp8(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                            int32_t num_tokens, int32_t max_q_len,
+                                            int32_t max_seq_len, const void* q,
+                                            const void* k_cache, const void* v_cache,
+                                            float k_scale, float v_scale,
+                                            const int32_t* block_table,
+                                            int32_t max_blocks_per_seq,
+                                            const int32_t* cu_seqlens_q,
+                                            const int32_t* seq_lens, const void* bias, void* out,
+                                            float* lse, int32_t num_splits, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  const float scales[2] = {k_scale, v_scale};
+  return decode_mq_common(desc, num_seqs, num_tokens, max_q_len, max_seq_len, q, k_cache,
+                          v_cache, block_table, max_blocks_per_seq, cu_seqlens_q, seq_lens, bias,
+                          out, lse, num_splits, workspace, workspace_bytes, scales, stream);
 }
 
 }  // extern "C"

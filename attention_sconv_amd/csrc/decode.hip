@@ -51,14 +51,32 @@ constexpr int kMaxTilesPerGroup = 3;
 // decode and fp32 use <8, 1>.  bf16 with several tiles uses 4 waves (one per
 // SIMD, so a wave may hold up to 512 registers) and keeps every tile's state
 // in the same wave, so each K/V fragment it loads serves all of its tiles.
-template <typename T, int kW, int kCT>
+// Raw K/V registers of one item: the operand fragments themselves for a
+// cache in the activation type; for an E4M3 cache the codes, 8 per fragment
+// (K: this lane's 32 dims of its 2 keys, two 16-byte loads per key; V^T:
+// 8 tokens of one dim, one 8-byte load per dim tile), converted to bf16
+// fragments when the item is processed.
+template <typename T, typename TKV> struct ItemRegs {
+  Frag8<T> k[8], v[8];
+};
+template <> struct ItemRegs<bf16, fp8e4> {
+  u32x4 k[4];
+  u32x2 v[8];
+};
+
+// TKV: the cache element type, T or fp8e4 (bf16 queries only).  An E4M3 cache
+// holds keys / k_scale and values / v_scale: the scores take k_scale with the
+// 1/sqrt(128) factor and the output takes v_scale (1 for other caches).
+template <typename T, typename TKV, int kW, int kCT>
 __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
     int Hq, int Hkv, int window, int R, int S, int n_cg, int B, const T* __restrict__ q,
-    const T* __restrict__ k_cache, const T* __restrict__ v_cache,
+    const TKV* __restrict__ k_cache, const TKV* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const T* __restrict__ bias,
     float* __restrict__ part_o, float* __restrict__ part_lse, T* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, float k_scale, float v_scale) {
+  constexpr bool kFp8 = std::is_same<TKV, fp8e4>::value;
+  static_assert(!kFp8 || std::is_same<T, bf16>::value, "E4M3 cache with bf16 queries");
   constexpr int kThr = 64 * kW;
   __shared__ float sm_m[kW][16];
   __shared__ float sm_l[kW][16];
@@ -121,17 +139,20 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
     pos[u] = pos0 + token;
     k_lo[u] = window > 0 ? max(0, pos[u] - window + 1) : 0;
     bias_row[u] = (uint32_t)h * (uint32_t)R;
+    // k-step ds of lane group grp contracts dims 32ds+8grp .. +7; with an
+    // E4M3 cache the dims are dealt 32grp+8ds .. +7 instead, so that a lane's
+    // four k-steps are 32 consecutive bytes of a key row.
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds)
       qf[u][ds] = head_ok[u] ? Frag8<T>::load(q + ((size_t)(tok0 + token) * Hq + h) * kHeadDim +
-                                              32 * ds + 8 * grp)
+                                              (kFp8 ? 32 * grp + 8 * ds : 32 * ds + 8 * grp))
                              : Frag8<T>::zero();
     m[u] = -INFINITY;
     l[u] = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[u][dt] = f32x4{0, 0, 0, 0};
   }
-  const float c = 0.08838834764831845f * kLog2e;   // log2(e) / sqrt(128)
+  const float c = 0.08838834764831845f * kLog2e * k_scale;   // log2(e) / sqrt(128)
 
   auto page_base = [&](int blk) -> size_t {
     const int phys = block_table[(size_t)b * max_blocks + blk];
@@ -148,10 +169,12 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
   // Each page is read through a buffer descriptor of its own; the quarter
   // and the dim tile are wave-uniform offsets, so the only per-lane address
   // state is one fixed byte offset for K and one for V^T.
-  constexpr uint32_t kPageBytes = kPage * kHeadDim * sizeof(T);
-  const uint32_t k_lane = ((8 * (col >> 2) + (col & 3)) * kHeadDim + 8 * grp) * sizeof(T);
-  const uint32_t v_lane = (col * kPage + 8 * grp) * sizeof(T);
-  auto load_item = [&](int item, Frag8<T>* kf, Frag8<T>* vf, T (*bb)[8]) {
+  constexpr uint32_t kPageBytes = kPage * kHeadDim * sizeof(TKV);
+  const uint32_t k_lane =
+      ((8 * (col >> 2) + (col & 3)) * kHeadDim + (kFp8 ? 32 : 8) * grp) * sizeof(TKV);
+  const uint32_t v_lane = (col * kPage + 8 * grp) * sizeof(TKV);
+  using Regs = ItemRegs<T, TKV>;
+  auto load_item = [&](int item, Regs& ir, T (*bb)[8]) {
     const int blk = my_lo + (item >> 2);
     const int qu = item & 3;
     const int j0 = blk * kPage + 32 * qu + 8 * grp;
@@ -164,22 +187,54 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
     const size_t base = page_base(blk);
     const rsrc_t kr = make_rsrc(k_cache + base, kPageBytes);
     const rsrc_t vr = make_rsrc(v_cache + base, kPageBytes);
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds)
-        kf[t * 4 + ds] = Frag8<T>::load(kr, k_lane + (4 * t * kHeadDim + 32 * ds) * sizeof(T),
-                                        32 * qu * kHeadDim * sizeof(T));
+        for (int hh = 0; hh < 2; ++hh)
+          ir.k[t * 2 + hh] = buf_load16(kr, k_lane + 4 * t * kHeadDim + 16 * hh,
+                                        32 * qu * kHeadDim);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      vf[dt] = Frag8<T>::load(vr, v_lane, (32 * qu + 16 * dt * kPage) * sizeof(T));
+      for (int dt = 0; dt < 8; ++dt)
+        ir.v[dt] = buf_load8(vr, v_lane, 32 * qu + 16 * dt * kPage);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds)
+          ir.k[t * 4 + ds] = Frag8<T>::load(kr, k_lane + (4 * t * kHeadDim + 32 * ds) * sizeof(T),
+                                            32 * qu * kHeadDim * sizeof(T));
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        ir.v[dt] = Frag8<T>::load(vr, v_lane, (32 * qu + 16 * dt * kPage) * sizeof(T));
+    }
+  };
+  // Operand fragment (t, ds) of K and dim tile dt of V^T.
+  auto k_frag = [&](const Regs& ir, int t, int ds) -> Frag8<T> {
+    if constexpr (kFp8) {
+      const u32x4& w = ir.k[t * 2 + (ds >> 1)];
+      return fp8x8_to_bf16(w[2 * (ds & 1)], w[2 * (ds & 1) + 1]);
+    } else {
+      return ir.k[t * 4 + ds];
+    }
+  };
+  auto v_frag = [&](const Regs& ir, int dt) -> Frag8<T> {
+    if constexpr (kFp8) return fp8x8_to_bf16(ir.v[dt][0], ir.v[dt][1]);
+    else return ir.v[dt];
   };
 
   // One item of 32 keys, for every column tile: scores, online softmax,
   // O^T += V^T P^T.
-  auto process_item = [&](int item, const Frag8<T>* kf, Frag8<T>* vf, const T (*bb)[8]) {
+  auto process_item = [&](int item, Regs& ir, const T (*bb)[8]) {
     const int blk = my_lo + (item >> 2);
     const int j0 = blk * kPage + 32 * (item & 3) + 8 * grp;
+    Frag8<T> kf[8], vf[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) kf[t * 4 + ds] = k_frag(ir, t, ds);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) vf[dt] = v_frag(ir, dt);
 #pragma unroll
     for (int u = 0; u < kCT; ++u) {
       f32x4 sacc[2];
@@ -241,26 +296,26 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
   // loads; the last one or two rounds are peeled so that no load is issued
   // for a round that does not exist.  The barrier carries no memory fence:
   // it only holds waves together, it does not wait for their loads.
-  Frag8<T> ka[8], va[8], kb[8], vb[8];
+  Regs ra, rb;
   T ba[kCT][8], bbb[kCT][8];
   const int rounds = (n_items + kW - 1) / kW;
   auto item_of = [&](int r) { return min(r * kW + wave, n_items - 1); };
   auto has_item = [&](int r) { return r * kW + wave < n_items; };
-  if (rounds > 0) load_item(item_of(0), ka, va, ba);
+  if (rounds > 0) load_item(item_of(0), ra, ba);
   int r = 0;
   for (; r + 2 < rounds; r += 2) {
-    load_item(item_of(r + 1), kb, vb, bbb);
-    process_item(item_of(r), ka, va, ba);      // rounds before the last are full
-    load_item(item_of(r + 2), ka, va, ba);
-    process_item(item_of(r + 1), kb, vb, bbb);
+    load_item(item_of(r + 1), rb, bbb);
+    process_item(item_of(r), ra, ba);          // rounds before the last are full
+    load_item(item_of(r + 2), ra, ba);
+    process_item(item_of(r + 1), rb, bbb);
     __builtin_amdgcn_s_barrier();
   }
   if (r + 1 < rounds) {
-    load_item(item_of(r + 1), kb, vb, bbb);
-    process_item(item_of(r), ka, va, ba);
-    if (has_item(r + 1)) process_item(item_of(r + 1), kb, vb, bbb);
+    load_item(item_of(r + 1), rb, bbb);
+    process_item(item_of(r), ra, ba);
+    if (has_item(r + 1)) process_item(item_of(r + 1), rb, bbb);
   } else if (r < rounds && has_item(r)) {
-    process_item(item_of(r), ka, va, ba);
+    process_item(item_of(r), ra, ba);
   }
 
   // Merge the waves, one column tile at a time.  O^T register r of tile dt
@@ -307,10 +362,10 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
       if (S == 1) {
         // A single split is the whole key range: write the result directly
         // (no merge pass).
-        out[orow * kHeadDim + d] = from_f32<T>(num / den);
+        out[orow * kHeadDim + d] = from_f32<T>(num / den * v_scale);
         if (lse != nullptr && d == 0) lse[orow] = (M + fast_log2(den)) * kLn2;
       } else {
-        part_o[row * kHeadDim + d] = num / den;
+        part_o[row * kHeadDim + d] = num / den * v_scale;
         if (d == 0) part_lse[row] = (M + fast_log2(den)) * kLn2;
       }
     }
@@ -341,20 +396,21 @@ __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(
 
 }  // namespace
 
-template <typename T, int kW, int kCT>
+template <typename T, typename TKV, int kW, int kCT>
 void launch_split(const AttnShape& s, int num_seqs, int num_splits, int n_cg, const void* q,
                   const void* k_cache, const void* v_cache, const int32_t* block_table,
                   int max_blocks_per_seq, const int32_t* cu_seqlens_q, const int32_t* seq_lens,
                   const void* bias, void* out, float* lse, float* part_o, float* part_lse,
-                  hipStream_t stream) {
+                  float k_scale, float v_scale, hipStream_t stream) {
   // One work-group per (split, kv-head, sequence) x column group, in groups
   // of 8 (see the kernel's id mapping).
   const long rest = (long)num_splits * s.Hkv * num_seqs;
-  hipLaunchKernelGGL((decode_split_kernel<T, kW, kCT>), dim3((unsigned)((rest + 7) / 8 * 8 * n_cg)),
-                     dim3(64 * kW), 0, stream, s.Hq, s.Hkv, s.window, s.bias_len, num_splits,
-                     n_cg, num_seqs, (const T*)q, (const T*)k_cache, (const T*)v_cache,
-                     block_table, max_blocks_per_seq, cu_seqlens_q, seq_lens, (const T*)bias,
-                     part_o, part_lse, (T*)out, lse);
+  hipLaunchKernelGGL((decode_split_kernel<T, TKV, kW, kCT>),
+                     dim3((unsigned)((rest + 7) / 8 * 8 * n_cg)), dim3(64 * kW), 0, stream, s.Hq,
+                     s.Hkv, s.window, s.bias_len, num_splits, n_cg, num_seqs, (const T*)q,
+                     (const TKV*)k_cache, (const TKV*)v_cache, block_table, max_blocks_per_seq,
+                     cu_seqlens_q, seq_lens, (const T*)bias, part_o, part_lse, (T*)out, lse,
+                     k_scale, v_scale);
 }
 
 template <typename T>
@@ -369,33 +425,42 @@ hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_tokens, int m
                          const void* v_cache, const int32_t* block_table,
                          int max_blocks_per_seq, const int32_t* cu_seqlens_q,
                          const int32_t* seq_lens, const void* bias, void* out, float* lse,
-                         float* part_o, float* part_lse, hipStream_t stream) {
+                         float* part_o, float* part_lse, const float* fp8_scales,
+                         hipStream_t stream) {
   const int n_ct = decode_column_tiles(s.Hq / s.Hkv, max_q_len);
+  const float ks = fp8_scales ? fp8_scales[0] : 1.0f;
+  const float vs = fp8_scales ? fp8_scales[1] : 1.0f;
   if (s.dtype == kDtypeBf16) {
-    if (n_ct == 1) {
-      launch_split<bf16, 8, 1>(s, num_seqs, num_splits, 1, q, k_cache, v_cache, block_table,
-                               max_blocks_per_seq, cu_seqlens_q, seq_lens, bias, out, lse,
-                               part_o, part_lse, stream);
-    } else {
-      // Several column tiles: up to kMaxTilesPerGroup per work-group, spread
-      // evenly over the fewest groups.
-      const int n_cg = (n_ct + kMaxTilesPerGroup - 1) / kMaxTilesPerGroup;
-      const int per = (n_ct + n_cg - 1) / n_cg;
-      auto go = [&](auto tag) {
-        constexpr int kCT = decltype(tag)::value;
-        launch_split<bf16, 4, kCT>(s, num_seqs, num_splits, n_cg, q, k_cache, v_cache,
-                                   block_table, max_blocks_per_seq, cu_seqlens_q, seq_lens,
-                                   bias, out, lse, part_o, part_lse, stream);
-      };
-      static_assert(kMaxTilesPerGroup == 3, "instantiations below");
-      if (per == 2) go(std::integral_constant<int, 2>{});
-      else go(std::integral_constant<int, 3>{});
-    }
+    auto bf16_path = [&](auto kv_tag) {
+      using TKV = decltype(kv_tag);
+      if (n_ct == 1) {
+        launch_split<bf16, TKV, 8, 1>(s, num_seqs, num_splits, 1, q, k_cache, v_cache,
+                                      block_table, max_blocks_per_seq, cu_seqlens_q, seq_lens,
+                                      bias, out, lse, part_o, part_lse, ks, vs, stream);
+      } else {
+        // Several column tiles: up to kMaxTilesPerGroup per work-group, spread
+        // evenly over the fewest groups.
+        const int n_cg = (n_ct + kMaxTilesPerGroup - 1) / kMaxTilesPerGroup;
+        const int per = (n_ct + n_cg - 1) / n_cg;
+        auto go = [&](auto tag) {
+          constexpr int kCT = decltype(tag)::value;
+          launch_split<bf16, TKV, 4, kCT>(s, num_seqs, num_splits, n_cg, q, k_cache, v_cache,
+                                          block_table, max_blocks_per_seq, cu_seqlens_q,
+                                          seq_lens, bias, out, lse, part_o, part_lse, ks, vs,
+                                          stream);
+        };
+        static_assert(kMaxTilesPerGroup == 3, "instantiations below");
+        if (per == 2) go(std::integral_constant<int, 2>{});
+        else go(std::integral_constant<int, 3>{});
+      }
+    };
+    if (fp8_scales != nullptr) bf16_path(fp8e4{});
+    else bf16_path(bf16{});
     if (num_splits > 1) launch_merge<bf16>(s, num_tokens, num_splits, part_o, part_lse, out, lse, stream);
   } else {
-    launch_split<float, 8, 1>(s, num_seqs, num_splits, n_ct, q, k_cache, v_cache, block_table,
-                              max_blocks_per_seq, cu_seqlens_q, seq_lens, bias, out, lse, part_o,
-                              part_lse, stream);
+    launch_split<float, float, 8, 1>(s, num_seqs, num_splits, n_ct, q, k_cache, v_cache,
+                                     block_table, max_blocks_per_seq, cu_seqlens_q, seq_lens,
+                                     bias, out, lse, part_o, part_lse, 1.0f, 1.0f, stream);
     if (num_splits > 1) launch_merge<float>(s, num_tokens, num_splits, part_o, part_lse, out, lse, stream);
   }
   return hipGetLastError();

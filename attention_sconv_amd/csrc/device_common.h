@@ -27,6 +27,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct bf16 { uint16_t bits; };
 
@@ -183,8 +184,37 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
 __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+
+// ---------------------------------------------------------------- fp8 KV cache
+// An FP8 cache element holds an OCP E4M3 code (1 sign, 4 exponent bits with
+// bias 7, 3 mantissa bits; largest finite value 448, no infinity) of the
+// value divided by the cache's scale.  Every E4M3 value is exactly a bf16.
+struct fp8e4 { uint8_t bits; };
+constexpr float kFp8Max = 448.0f;
+
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+// Four fp32 values -> four E4M3 codes in one word (byte e holds value e):
+// clamped to +-448 first (saturation), then rounded to nearest even by
+// v_cvt_pk_fp8_f32.
+__device__ __forceinline__ uint32_t fp8x4_from_f32(float a, float b, float c, float d) {
+  const auto sat = [](float x) { return fminf(fmaxf(x, -kFp8Max), kFp8Max); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+  return (uint32_t)w;
+}
+// Eight E4M3 codes (byte e of word e/4 is element e) -> the bf16 fragment of
+// their values, exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1).
+__device__ __forceinline__ Frag8<bf16> fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  Frag8<bf16> f;
+  f.v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  f.v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  f.v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  f.v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  return f;
 }
 
 // 32x32 output, contracts 16 k-values (lane group lane/32 holds k = 8G..8G+7).

@@ -11,11 +11,14 @@ namespace inkattn {
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBf16 = 1;
 
+// fp8_scales: host pointer to {key scale, value scale} for an E4M3 cache, or
+// nullptr for a cache in the activation dtype.
 hipError_t launch_sconv(int dtype, int Hkv, int num_seqs, int max_chunk_len,
                         const void* k_in, const void* v_in, const void* conv_w,
                         void* conv_state, const int32_t* state_slot,
                         const int32_t* cu_seqlens, const int32_t* slot_mapping,
-                        void* k_cache, void* v_cache, hipStream_t stream);
+                        void* k_cache, void* v_cache, const float* fp8_scales,
+                        hipStream_t stream);
 
 hipError_t launch_sconv_paged(int dtype, int Hkv, int num_seqs, int max_chunk_len,
                               const void* k_in, const void* v_in, const void* conv_w,
@@ -41,7 +44,8 @@ hipError_t launch_prefill(const AttnShape& s, int num_seqs, int max_q_len, const
 // Decode over num_seqs sequences with 1 .. max_q_len query tokens each
 // (cu_seqlens_q == nullptr: exactly one token per sequence, token b of
 // sequence b).  The (token, head) columns of a kv-head group are computed in
-// tiles of 16 by separate work-groups.
+// tiles of 16.  fp8_scales: host pointer to {key scale, value scale} for an
+// E4M3 cache (bf16 queries), or nullptr for a cache in the activation dtype.
 constexpr int decode_column_tiles(int G, int max_q_len) { return (G * max_q_len + 15) / 16; }
 
 hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_tokens, int max_q_len,
@@ -49,6 +53,7 @@ hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_tokens, int m
                          const void* v_cache, const int32_t* block_table,
                          int max_blocks_per_seq, const int32_t* cu_seqlens_q,
                          const int32_t* seq_lens, const void* bias, void* out, float* lse,
-                         float* part_o, float* part_lse, hipStream_t stream);
+                         float* part_o, float* part_lse, const float* fp8_scales,
+                         hipStream_t stream);
 
 }  // namespace inkattn

@@ -26,6 +26,8 @@
 // be evicted, and prefix caching covers the sconv state too).  A chunk at
 // positions ctx .. ctx+n-1 reads its halo ctx-3 .. ctx-1 from there (zero
 // before position 0) and writes its own rows there.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -43,13 +45,16 @@ struct SconvPaged {
   void* v_state;                  // [blocks][128][C] pre-convolution values
 };
 
-template <typename T, bool kPaged>
+// FP8 cache (TC = fp8e4): the outputs are stored as E4M3 codes of y / scale;
+// inv_scale[0|1] = 1 / scale of the key | value cache.
+template <typename T, typename TC, bool kPaged>
 __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
     int C, int Hkv, const T* __restrict__ k_in, const T* __restrict__ v_in,
     const T* __restrict__ conv_w, T* __restrict__ conv_state,
     const int32_t* __restrict__ state_slot, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ slot_mapping, T* __restrict__ k_cache,
-    T* __restrict__ v_cache, SconvPaged pg) {
+    const int32_t* __restrict__ slot_mapping, TC* __restrict__ k_cache,
+    TC* __restrict__ v_cache, SconvPaged pg, float inv_scale_k, float inv_scale_v) {
+  constexpr bool kFp8 = std::is_same<TC, fp8e4>::value;
   const int which = blockIdx.z;              // 0 = keys, 1 = values
   const int b = blockIdx.y;
   const int r0 = (blockIdx.x * blockDim.y + threadIdx.y) * kSconvTok;   // first token (relative)
@@ -110,12 +115,30 @@ __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
 
   const int kvh = c0 / kHeadDim;
   const int dd = c0 % kHeadDim;
+  // 8 outputs -> 8 cache elements at p (one 16-byte bf16 / 32-byte fp32
+  // store, or 8 E4M3 codes in one 8-byte store).
+  const float inv = which ? inv_scale_v : inv_scale_k;
+  auto store8 = [&](TC* p, const float* v8) {
+    if constexpr (kFp8) {
+      *reinterpret_cast<u32x2*>(p) =
+          u32x2{fp8x4_from_f32(v8[0] * inv, v8[1] * inv, v8[2] * inv, v8[3] * inv),
+                fp8x4_from_f32(v8[4] * inv, v8[5] * inv, v8[6] * inv, v8[7] * inv)};
+    } else {
+      Frag8<T>::pack(v8).store(p);
+    }
+  };
+  auto store1 = [&](TC* p, float v) {
+    if constexpr (kFp8)
+      *p = fp8e4{(uint8_t)(fp8x4_from_f32(v * inv, 0.0f, 0.0f, 0.0f) & 0xffu)};
+    else
+      *p = from_f32<T>(v);
+  };
   if (which == 0) {
 #pragma unroll
     for (int t = 0; t < kSconvTok; ++t) {
       if (slot[t] < 0) continue;
       const size_t tile = (size_t)(slot[t] >> 7) * Hkv + kvh;
-      Frag8<T>::pack(y[t]).store(k_cache + (tile * kPage + (slot[t] & (kPage - 1))) * kHeadDim + dd);
+      store8(k_cache + (tile * kPage + (slot[t] & (kPage - 1))) * kHeadDim + dd, y[t]);
     }
   } else {
     // V is stored transposed per page.  When the 8 tokens occupy 8
@@ -127,22 +150,22 @@ __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
     for (int t = 1; t < kSconvTok; ++t) run = run && slot[t] == slot[0] + t;
     if (run) {
       const size_t tile = (size_t)(slot[0] >> 7) * Hkv + kvh;
-      T* vt = v_cache + (tile * kHeadDim + dd) * kPage + (slot[0] & (kPage - 1));
+      TC* vt = v_cache + (tile * kHeadDim + dd) * kPage + (slot[0] & (kPage - 1));
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float col[kSconvTok];
 #pragma unroll
         for (int t = 0; t < kSconvTok; ++t) col[t] = y[t][e];
-        Frag8<T>::pack(col).store(vt + (size_t)e * kPage);
+        store8(vt + (size_t)e * kPage, col);
       }
     } else {
 #pragma unroll
       for (int t = 0; t < kSconvTok; ++t) {
         if (slot[t] < 0) continue;
         const size_t tile = (size_t)(slot[t] >> 7) * Hkv + kvh;
-        T* vt = v_cache + (tile * kHeadDim + dd) * kPage + (slot[t] & (kPage - 1));
+        TC* vt = v_cache + (tile * kHeadDim + dd) * kPage + (slot[t] & (kPage - 1));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vt[(size_t)e * kPage] = from_f32<T>(y[t][e]);
+        for (int e = 0; e < 8; ++e) store1(vt + (size_t)e * kPage, y[t][e]);
       }
     }
   }
@@ -255,7 +278,7 @@ hipError_t launch_sconv_any(int dtype, int Hkv, int num_seqs, int max_chunk_len,
                             void* conv_state, const int32_t* state_slot,
                             const int32_t* cu_seqlens, const int32_t* slot_mapping,
                             void* k_cache, void* v_cache, const SconvPaged& pg,
-                            hipStream_t stream) {
+                            const float* fp8_scales, hipStream_t stream) {
   const int C = Hkv * kHeadDim;
   const int per_block = kSconvTok * kSconvRows;
   dim3 grid((max_chunk_len + per_block - 1) / per_block, num_seqs, 2);
@@ -264,17 +287,25 @@ hipError_t launch_sconv_any(int dtype, int Hkv, int num_seqs, int max_chunk_len,
     block.y = 1024 / block.x;
     grid.x = (max_chunk_len + kSconvTok * block.y - 1) / (kSconvTok * block.y);
   }
-  if (dtype == kDtypeBf16) {
-    hipLaunchKernelGGL((sconv_cache_write_kernel<bf16, kPaged>), grid, block, 0, stream, C, Hkv,
-                       (const bf16*)k_in, (const bf16*)v_in, (const bf16*)conv_w,
-                       (bf16*)conv_state, state_slot, cu_seqlens, slot_mapping,
-                       (bf16*)k_cache, (bf16*)v_cache, pg);
-  } else {
-    hipLaunchKernelGGL((sconv_cache_write_kernel<float, kPaged>), grid, block, 0, stream, C, Hkv,
-                       (const float*)k_in, (const float*)v_in, (const float*)conv_w,
-                       (float*)conv_state, state_slot, cu_seqlens, slot_mapping,
-                       (float*)k_cache, (float*)v_cache, pg);
+  auto go = [&](auto t_tag, auto c_tag) {
+    using T = decltype(t_tag);
+    using TC = decltype(c_tag);
+    const float ik = fp8_scales ? 1.0f / fp8_scales[0] : 1.0f;
+    const float iv = fp8_scales ? 1.0f / fp8_scales[1] : 1.0f;
+    hipLaunchKernelGGL((sconv_cache_write_kernel<T, TC, kPaged>), grid, block, 0, stream, C,
+                       Hkv, (const T*)k_in, (const T*)v_in, (const T*)conv_w, (T*)conv_state,
+                       state_slot, cu_seqlens, slot_mapping, (TC*)k_cache, (TC*)v_cache, pg,
+                       ik, iv);
+  };
+  if constexpr (!kPaged) {
+    if (fp8_scales != nullptr) {
+      if (dtype == kDtypeBf16) go(bf16{}, fp8e4{});
+      else go(0.0f, fp8e4{});
+      return hipGetLastError();
+    }
   }
+  if (dtype == kDtypeBf16) go(bf16{}, bf16{});
+  else go(0.0f, 0.0f);
   return hipGetLastError();
 }
 
@@ -282,11 +313,12 @@ hipError_t launch_sconv(int dtype, int Hkv, int num_seqs, int max_chunk_len,
                         const void* k_in, const void* v_in, const void* conv_w,
                         void* conv_state, const int32_t* state_slot,
                         const int32_t* cu_seqlens, const int32_t* slot_mapping,
-                        void* k_cache, void* v_cache, hipStream_t stream) {
+                        void* k_cache, void* v_cache, const float* fp8_scales,
+                        hipStream_t stream) {
   return launch_sconv_any<false>(dtype, Hkv, num_seqs, max_chunk_len, k_in, v_in, conv_w,
                                  conv_state, state_slot, cu_seqlens, slot_mapping, k_cache,
                                  v_cache, SconvPaged{nullptr, nullptr, 0, nullptr, nullptr},
-                                 stream);
+                                 fp8_scales, stream);
 }
 
 hipError_t launch_sconv_paged(int dtype, int Hkv, int num_seqs, int max_chunk_len,
@@ -299,7 +331,7 @@ hipError_t launch_sconv_paged(int dtype, int Hkv, int num_seqs, int max_chunk_le
                                 nullptr, nullptr, cu_seqlens, slot_mapping, k_cache, v_cache,
                                 SconvPaged{seq_lens, state_block_table, max_state_blocks,
                                            k_state, v_state},
-                                stream);
+                                nullptr, stream);
 }
 
 }  // namespace inkattn

@@ -15,6 +15,9 @@ HEAD_DIM = 128
 
 
 def torch_dtype(dtype):
+    """Cache element type: bf16 / fp32, or "fp8" (E4M3 codes held as uint8)."""
+    if dtype == "fp8":
+        return torch.uint8
     return torch.bfloat16 if dtype in (1, "bf16") else torch.float32
 
 

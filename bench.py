@@ -51,10 +51,11 @@ def valid_pairs(q_len, seq_len, window):
 class DeviceCase:
     """Device tensors of one synth case in the library's layouts."""
 
-    def __init__(self, case, torch):
+    def __init__(self, case, torch, fp8_scales=None):
         import attention_sconv_amd as ink
         from attention_sconv_amd import kvcache
         self.case = c = case
+        self.fp8 = fp8_scales
         td = torch.bfloat16 if c.dtype == "bf16" else torch.float32
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(td)
         idev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
@@ -67,11 +68,17 @@ class DeviceCase:
         if c.past_k is not None:
             pk = c.past_k if torch.is_tensor(c.past_k) else dev(c.past_k)
             pv = c.past_v if torch.is_tensor(c.past_v) else dev(c.past_v)
+            if fp8_scales:
+                # the cached context as E4M3 codes (torch's float8_e4m3fn cast)
+                pk, pv = [(x.float() / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+                          .view(torch.uint8) for x, s in ((pk, fp8_scales[0]),
+                                                          (pv, fp8_scales[1]))]
             self.k_cache, self.v_cache = kvcache.from_slots(pk, pv)
             del pk, pv
             c.past_k = c.past_v = None
         else:
-            self.k_cache, self.v_cache = kvcache.alloc(c.num_blocks, c.num_kv_heads, c.dtype)
+            self.k_cache, self.v_cache = kvcache.alloc(c.num_blocks, c.num_kv_heads,
+                                                       "fp8" if fp8_scales else c.dtype)
             self.k_cache.zero_()
             self.v_cache.zero_()
         self.out = torch.empty_like(self.q)
@@ -80,6 +87,13 @@ class DeviceCase:
 
     def sconv(self):
         c = self.case
+        if self.fp8:
+            self.ink.inkattn_sconv_fp8(self.dt, c.num_kv_heads, HEAD_DIM, len(c.q_lens),
+                                       c.num_tokens, int(c.q_lens.max()), self.k_pre,
+                                       self.v_pre, self.conv_w, self.conv_state,
+                                       self.state_slot, self.cu, self.slot_mapping,
+                                       self.fp8[0], self.fp8[1], self.k_cache, self.v_cache)
+            return
         self.ink.inkattn_sconv(self.dt, c.num_kv_heads, HEAD_DIM, len(c.q_lens), c.num_tokens,
                                int(c.q_lens.max()), self.k_pre, self.v_pre, self.conv_w,
                                self.conv_state, self.state_slot, self.cu, self.slot_mapping,
@@ -114,6 +128,16 @@ class DeviceCase:
         self.ws_bytes = self.ink.inkattn_relattn_decode_mq_workspace_size(
             self.desc, B, c.num_tokens, Q, L, 0)
         self.ws = torch.empty(self.ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
+
+    def decode_fp8(self):
+        c = self.case
+        self.ink.inkattn_relattn_decode_fp8(self.desc, len(c.q_lens), c.num_tokens,
+                                            int(c.q_lens.max()), int(c.seq_lens.max()), self.q,
+                                            self.k_cache, self.v_cache, self.fp8[0],
+                                            self.fp8[1], self.block_table,
+                                            self.block_table.shape[1], self.cu, self.seq_lens,
+                                            self.bias, self.out, None, 0, self.ws,
+                                            self.ws_bytes)
 
     def decode_mq(self):
         c = self.case
@@ -268,6 +292,8 @@ def main():
     ap.add_argument("--no-mtp", action="store_true",
                     help="skip the MTP-verification decode leg (it launches the decode kernel "
                          "with another shape)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the decode leg with an FP8 (E4M3) KV cache")
     ap.add_argument("--no-sconv-out", action="store_true",
                     help="skip the leg that times the sconv of a plain activation tensor")
     ap.add_argument("--steady-s", type=float, default=0.3,
@@ -429,6 +455,44 @@ def main():
                     "per 16 (token, head) columns",
         }
         del md
+
+    # ---------------- FP8 (E4M3) KV cache: the 16K SWA decode step again
+    if not args.no_decode and not args.no_fp8:
+        fcase = synth.workload_case(dwl, seed=0, past_device="cuda")
+        fd = DeviceCase(fcase, torch, fp8_scales=(1 / 64, 1 / 64))
+        fd.setup_decode_mq(torch)
+        f_bytes = kv_bytes // 2
+
+        def fstep(ev):
+            fd.sconv()
+            if ev is not None:
+                ev[0].record()
+            fd.decode_fp8()
+            if ev is not None:
+                ev[1].record()
+
+        print(f"[bench] decode {dwl.name} with an FP8 cache", file=sys.stderr, flush=True)
+        steady_clocks(torch, fstep, args.steady_s)
+        f8_ms_step, f8ks = time_region(torch, fstep, None, d_steps, args.warmup)
+        f8_ms = sum(f8ks) / len(f8ks)
+        f8_gbs = f_bytes / (f8_ms * 1e-3) / 1e9
+        result["decode_fp8"] = {
+            "workload": dwl.name + " with an E4M3 KV cache (scales 1/64)",
+            "ms_per_step": round(f8_ms_step, 4), "ms_decode": round(f8_ms, 4),
+            "ms_decode_median": round(float(np.median(f8ks)), 4),
+            "num_splits": fd.num_splits, "kv_bytes": f_bytes,
+            "achieved": round(f8_gbs, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
+            "frac": round(f8_gbs / PEAK_HBM_GBS, 4),
+            "speedup_vs_bf16_cache": round(d_ms / f8_ms, 3),
+            "traffic": recorded_traffic(
+                "decode_split_fp8_swa_decode_16k.traffic.txt",
+                ["attention_sconv_amd/csrc/decode.hip",
+                 "attention_sconv_amd/csrc/device_common.h"]),
+            "note": "inkattn_sconv_fp8 + inkattn_relattn_decode_fp8; bytes = the E4M3 K+V "
+                    "in the attended range",
+        }
+        del fd
+        torch.cuda.empty_cache()
 
     import attention_sconv_amd as ink
     # ---------------- sconv of a plain activation (attention / MoE output)

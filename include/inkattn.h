@@ -254,6 +254,49 @@ inkattn_status_t inkattn_relattn_decode_mq(const inkattn_attn_desc_t* desc, int3
                                            int32_t num_splits, void* workspace,
                                            size_t workspace_bytes, void* stream);
 
+/* ---- FP8 KV cache ---------------------------------------------------------
+ * [A] Roadmap: FP8 for the global-attention layers, which are bound by
+ * compute and by KV-cache capacity.  An FP8 cache has the layout above with
+ * one byte per element (a 16 KiB tile per (block, kv-head)); each byte is the
+ * OCP E4M3 code (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinity; largest finite value 448) of the key divided by k_scale, or of
+ * the value divided by v_scale: one positive finite float scale per cache,
+ * chosen by the caller (for example max |x| / 448 over a calibration set).
+ * A cached element reads back as value(code) * scale.
+ *
+ * inkattn_sconv_fp8: inkattn_sconv writing an FP8 cache.  Each output is
+ * divided by its cache's scale (as a product with the fp32 reciprocal),
+ * clamped to +-448 and rounded to the nearest E4M3 value, ties to even.
+ * Inputs, taps and the sconv state keep the dtype (fp32 or bf16).  Errors as
+ * inkattn_sconv, plus INKATTN_EINVAL for a scale that is not positive and
+ * finite or whose reciprocal overflows. */
+inkattn_status_t inkattn_sconv_fp8(int32_t dtype, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_seqs, int32_t num_tokens, int32_t max_chunk_len,
+                                   const void* k_in, const void* v_in, const void* conv_w,
+                                   void* conv_state, const int32_t* state_slot,
+                                   const int32_t* cu_seqlens, const int32_t* slot_mapping,
+                                   float k_scale, float v_scale, void* k_cache, void* v_cache,
+                                   void* stream);
+
+/* inkattn_relattn_decode_mq over an FP8 cache: the same arguments and
+ * results, with the keys and values read back from their codes (k_scale,
+ * v_scale as written).  Queries, bias and out are bf16 (desc->dtype must be
+ * INKATTN_BF16, else INKATTN_ENOTSUP); one query token per sequence is the
+ * plain decode.  Split count and workspace size come from
+ * inkattn_relattn_decode_mq_num_splits / _workspace_size.  Errors as
+ * inkattn_relattn_decode_mq, plus INKATTN_EINVAL for a bad scale. */
+inkattn_status_t inkattn_relattn_decode_fp8(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                            int32_t num_tokens, int32_t max_q_len,
+                                            int32_t max_seq_len, const void* q,
+                                            const void* k_cache, const void* v_cache,
+                                            float k_scale, float v_scale,
+                                            const int32_t* block_table,
+                                            int32_t max_blocks_per_seq,
+                                            const int32_t* cu_seqlens_q,
+                                            const int32_t* seq_lens, const void* bias, void* out,
+                                            float* lse, int32_t num_splits, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* inkattn_status_string(int32_t status);
 

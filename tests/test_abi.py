@@ -252,3 +252,51 @@ def _sconv_out(**kw):
 ])
 def test_sconv_out_host_validation(kw, status):
     assert _sconv_out(**kw) == status
+
+
+def _sconv_fp8(**kw):
+    args = dict(dtype=ink.BF16, Hkv=4, d=128, seqs=2, toks=10, maxlen=8, k=FAKE, v=FAKE,
+                w=FAKE, st=FAKE, slot=FAKE, cu=FAKE, sm=FAKE, ks=0.02, vs=0.03, kc=FAKE,
+                vc=FAKE)
+    args.update(kw)
+    return ink._lib._lib.inkattn_sconv_fp8(
+        args["dtype"], args["Hkv"], args["d"], args["seqs"], args["toks"], args["maxlen"],
+        args["k"], args["v"], args["w"], args["st"], args["slot"], args["cu"], args["sm"],
+        args["ks"], args["vs"], args["kc"], args["vc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), 2), (dict(d=64), 2), (dict(Hkv=0), 1), (dict(seqs=0), 0),
+    (dict(toks=0), 0), (dict(ks=0.0), 1), (dict(vs=-1.0), 1), (dict(ks=float("inf")), 1),
+    (dict(vs=float("nan")), 1), (dict(ks=1e-39), 1),            # reciprocal overflows
+    (dict(ks=0.0, seqs=0), 1),                                   # scales checked first
+    (dict(kc=None), 1), (dict(kc=FAKE + 8), 1),
+])
+def test_sconv_fp8_host_validation(kw, status):
+    assert _sconv_fp8(**kw) == status
+
+
+def _decode_fp8(desc, **kw):
+    args = dict(num_seqs=2, num_tokens=2, max_q_len=1, max_seq_len=100, q=FAKE, k=FAKE,
+                v=FAKE, ks=0.02, vs=0.03, bt=FAKE, mb=1, cu=FAKE, sl=FAKE, bias=FAKE, out=FAKE,
+                lse=None, splits=0, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    return ink._lib._lib.inkattn_relattn_decode_fp8(
+        ctypes.byref(desc), args["num_seqs"], args["num_tokens"], args["max_q_len"],
+        args["max_seq_len"], args["q"], args["k"], args["v"], args["ks"], args["vs"],
+        args["bt"], args["mb"], args["cu"], args["sl"], args["bias"], args["out"],
+        args["lse"], args["splits"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=0.0), 1), (dict(vs=float("inf")), 1), (dict(max_q_len=17), 2),
+    (dict(cu=None), 1), (dict(k=None), 1), (dict(ws_bytes=16), 1), (dict(num_seqs=0), 0),
+])
+def test_decode_fp8_host_validation(kw, status):
+    d = ink.make_desc(ink.BF16, 32, 4, 0, 128)
+    assert _decode_fp8(d, **kw) == status
+
+
+def test_decode_fp8_needs_bf16_queries():
+    d = ink.make_desc(ink.FP32, 32, 4, 0, 128)
+    assert _decode_fp8(d) == 2
