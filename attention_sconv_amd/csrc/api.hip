@@ -53,7 +53,8 @@ int64_t blocks_in_range(const inkattn_attn_desc_t* d, int64_t max_seq_len, int64
 int32_t auto_splits(const inkattn_attn_desc_t* d, int32_t num_seqs, int32_t max_seq_len,
                     int32_t max_q_len = 1) {
   const int64_t pairs = (int64_t)num_seqs * d->num_kv_heads *
-                        inkattn::decode_column_tiles(d->num_q_heads / d->num_kv_heads, max_q_len);
+                        inkattn::decode_groups_per_pair(d->dtype, d->num_q_heads / d->num_kv_heads,
+                                                        max_q_len);
   const int64_t nblk = blocks_in_range(d, max_seq_len, max_q_len);
   if (pairs <= 0 || nblk <= 0) return 1;
   int64_t s = (kDecodeTargetGroups + pairs - 1) / pairs;
@@ -74,7 +75,7 @@ bool decode_grid_too_large(const inkattn_attn_desc_t* d, int64_t num_seqs, int64
                            int32_t max_q_len) {
   const int64_t rest = splits * d->num_kv_heads * num_seqs;
   const int64_t n_ct = inkattn::decode_column_tiles(d->num_q_heads / d->num_kv_heads, max_q_len);
-  return (rest + 7) / 8 * 8 * n_ct > 0x7fffffffLL;
+  return (rest + 7) / 8 * 8 * n_ct > 0x7fffffffLL;   // (covers the LDS-staged grid, rest)
 }
 
 inkattn_status_t from_hip(hipError_t e) { return e == hipSuccess ? INKATTN_OK : INKATTN_EHIP; }

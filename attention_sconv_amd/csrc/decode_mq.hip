@@ -1,0 +1,365 @@
+// Multi-query split-K paged decode: several query tokens per sequence (the
+// verification of multi-token-prediction drafts), K/V staged through LDS.
+//
+// Source: news article "vLLM, TML Inkling Day-0 support", Model Architecture /
+// Attention (GQA, head size 128, sliding-window and full layers, a learned
+// relative-position term added to the logits), Model Architecture / MTP and
+// Performance (draft tokens verified in one step), and vLLM Integration &
+// Optimization / FA4 with sheared bias (the key range cut into splits).
+// Logit of query head h at position p against key j:
+//   q.k_j / sqrt(128) + bias[h][min(p - j, R - 1)].
+//
+// With n query tokens a kv-head group has n * Hq/Hkv (token, head) columns,
+// e.g. 72 for 9 tokens and 8 heads.  A kernel that keeps every column in
+// each wave's registers must read the K/V range once per few columns; here
+// one work-group of 8 waves per (split, kv-head, sequence) reads each K/V
+// byte of its range once:
+// * Units of 64 keys (half a page) go HBM -> registers -> LDS, every thread
+//   moving 16-byte chunks (coalesced: a wave load covers 1 KiB of a K page or
+//   eight 128-byte runs of its V^T rows).  Two units are in flight while a
+//   third is computed; one barrier per unit.  An E4M3 cache is converted to
+//   bf16 on its way into LDS, so both caches share the compute below.
+// * Wave w owns column tile w (columns 16w .. 16w+15, token = column / G,
+//   head = column % G) and runs, per unit, S^T = K Q^T and O^T += V^T P^T on
+//   v_mfma_f32_16x16x32_bf16 with its fragments read from LDS, and the online
+//   softmax of its columns over the unit's 64 keys.
+// * Sheared bias: the distances of a unit form, per head, a band of 63 + n
+//   entries; the band of every head of the group is staged with the unit
+//   (clamped at R - 1, pre-multiplied by log2 e) and read from LDS.
+// * K rows are stored in LDS with bits 2 and 4 of the key index swapped, so
+//   the 16 keys that a quarter-wave reads for one fragment sit in 16
+//   distinct bank groups (row stride 68 dwords); V^T rows (stride 36 dwords)
+//   are conflict-free as they are.
+// Keys past the sequence end exist only in its last page and may hold any
+// bits: their V^T columns are zeroed on the way into LDS and their logits are
+// masked, so 0 * NaN never reaches O.
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace inkattn {
+
+namespace {
+
+constexpr int kMqWaves = 8;
+constexpr int kMqThreads = 64 * kMqWaves;
+constexpr int kUnit = 64;                   // keys per staged unit (half a page)
+constexpr int kKRow = kHeadDim + 8;         // LDS K row, elements (68 dwords)
+constexpr int kVRow = kUnit + 8;            // LDS V^T row, elements (36 dwords)
+constexpr int kMaxG = 16;                   // q-heads per kv-head
+constexpr int kBandW = 80;                  // >= 63 + 16 distances per head and unit
+constexpr int kBandSlots = kMaxG * kBandW;  // staged bias entries per unit
+constexpr int kBandPer = (kBandSlots + kMqThreads - 1) / kMqThreads;
+
+struct MqSmem {
+  bf16 k[2][kUnit * kKRow];                 // [key (permuted)][d]
+  bf16 vt[2][kHeadDim * kVRow];             // [d][key]
+  float band[2][kBandSlots];                // [head in group][distance - d_min]
+};
+
+// LDS row, within its 32-key item, of key k (0 .. 31): bits 2 and 4 swapped.
+__device__ __forceinline__ int krow(int k) {
+  return (k & 0x0b) | ((k & 0x04) << 2) | ((k & 0x10) >> 2);
+}
+
+// A unit's raw chunks in flight: 16-byte chunks of K and of V^T per thread
+// (two each for bf16, one each for E4M3), and the thread's bias entries.
+template <typename TKV> struct MqStage {
+  static constexpr int kChunks = (int)sizeof(TKV);
+  u32x4 k[kChunks], v[kChunks];
+  bf16 bias[kBandPer];
+};
+
+// Barrier that publishes this wave's LDS writes but leaves its global loads
+// in flight (a fenced barrier would wait for those as well).  One asm
+// statement with a memory clobber, so no LDS access moves across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Sixteen E4M3 codes -> two bf16 fragments (elements 0-7 and 8-15), exactly.
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4& w, Frag8<bf16>& lo, Frag8<bf16>& hi) {
+  lo = fp8x8_to_bf16(w[0], w[1]);
+  hi = fp8x8_to_bf16(w[2], w[3]);
+}
+
+template <typename TKV>
+__global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
+    int Hq, int Hkv, int window, int R, int S, int B, const bf16* __restrict__ q,
+    const TKV* __restrict__ k_cache, const TKV* __restrict__ v_cache,
+    const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ seq_lens, const bf16* __restrict__ bias,
+    float* __restrict__ part_o, float* __restrict__ part_lse, bf16* __restrict__ out,
+    float* __restrict__ lse, float k_scale, float v_scale) {
+  constexpr bool kFp8 = std::is_same<TKV, fp8e4>::value;
+  constexpr int kSz = (int)sizeof(TKV);
+  constexpr int kKChunksPerRow = kHeadDim * kSz / 16;   // 16-byte chunks per K row
+  constexpr int kVChunksPerRow = kUnit * kSz / 16;      // ... per V^T row of a unit
+  constexpr int kEpc = 16 / kSz;                        // elements per chunk
+  constexpr uint32_t kPageBytes = kPage * kHeadDim * kSz;
+  __shared__ MqSmem sm;
+
+  const int id = blockIdx.x;
+  if (id >= S * Hkv * B) return;
+  const int split = id % S;
+  const int kvh = (id / S) % Hkv;
+  const int b = id / (S * Hkv);
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  const int tok0 = cu_q[b];
+  const int q_len = cu_q[b + 1] - tok0;
+  const int n_cols = G * q_len;
+  const int L = seq_lens[b];
+  const int pos0 = L - q_len;                    // position of the first query token
+  const int kstart = window > 0 ? max(0, pos0 - window + 1) : 0;
+  const int blk_first = kstart >> 7;
+  const int blk_last = (L - 1) >> 7;
+  const int nblk = blk_last - blk_first + 1;
+  const int bps = (nblk + S - 1) / S;
+  const int my_lo = blk_first + split * bps;
+  const int my_hi = min(my_lo + bps, blk_last + 1);
+  const int n_units = 2 * max(my_hi - my_lo, 0);
+
+  // This wave's column tile (wave-uniform: whether it has one at all).
+  const bool active = 16 * wave < n_cols;
+  const int gc = 16 * wave + col;
+  const bool head_ok = gc < n_cols;
+  const int token = head_ok ? gc / G : 0;
+  const int hl = head_ok ? gc % G : 0;           // head within the group
+  const int h = kvh * G + hl;
+  const int pos = pos0 + token;
+  const int k_lo = window > 0 ? max(0, pos - window + 1) : 0;
+  const float c = 0.08838834764831845f * kLog2e * k_scale;   // log2(e) / sqrt(128)
+
+  // Q^T fragments (B operand): k-step ds of lane group grp holds dims
+  // 32ds + 8grp .. +7.
+  Frag8<bf16> qf[4];
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds)
+    qf[ds] = head_ok ? Frag8<bf16>::load(q + ((size_t)(tok0 + token) * Hq + h) * kHeadDim +
+                                         32 * ds + 8 * grp)
+                     : Frag8<bf16>::zero();
+
+  // ---- staging.  Unit u is page my_lo + u/2, keys 64(u%2) .. +63 of it.
+  // Every load is unconditional (a unit index past the end re-reads the last
+  // unit) so that each wait the compiler places covers exactly the loads it
+  // needs and the next units stay in flight.
+  const rsrc_t bias_r = make_rsrc(bias, (uint32_t)((size_t)Hq * R * sizeof(bf16)));
+  auto unit_key0 = [&](int u) { return (my_lo + (u >> 1)) * kPage + kUnit * (u & 1); };
+  auto stage_load = [&](int u, MqStage<TKV>& st) {
+    u = min(u, n_units - 1);
+    const int blk = my_lo + (u >> 1);
+    const int phys = block_table[(size_t)b * max_blocks + blk];
+    const size_t base = ((size_t)phys * Hkv + kvh) * (size_t)(kPage * kHeadDim);
+    const rsrc_t kr = make_rsrc(k_cache + base, kPageBytes);
+    const rsrc_t vr = make_rsrc(v_cache + base, kPageBytes);
+    const uint32_t k_soff = (uint32_t)(kUnit * (u & 1) * kHeadDim * kSz);
+    const uint32_t v_soff = (uint32_t)(kUnit * (u & 1) * kSz);
+#pragma unroll
+    for (int i = 0; i < MqStage<TKV>::kChunks; ++i) {
+      const int ch = tid + kMqThreads * i;
+      const int key = ch / kKChunksPerRow, kc = ch % kKChunksPerRow;
+      st.k[i] = buf_load16(kr, (uint32_t)(key * kHeadDim * kSz + 16 * kc), k_soff);
+      const int d = ch / kVChunksPerRow, vc = ch % kVChunksPerRow;
+      st.v[i] = buf_load16(vr, (uint32_t)(d * kPage * kSz + 16 * vc), v_soff);
+    }
+    // Band of head e at offset v: distance d_min + v, d_min = pos0 - key0 - 63.
+    const int d_min = pos0 - unit_key0(u) - (kUnit - 1);
+#pragma unroll
+    for (int i = 0; i < kBandPer; ++i) {
+      const int s = min(tid + kMqThreads * i, G * kBandW - 1);
+      const int e = s / kBandW, v = s % kBandW;
+      const int dist = min(max(d_min + v, 0), R - 1);
+      st.bias[i] = buf_load_elem<bf16>(
+          bias_r, (uint32_t)(((kvh * G + e) * R + dist) * (int)sizeof(bf16)));
+    }
+  };
+  auto stage_store = [&](int u, const MqStage<TKV>& st, int buf) {
+    const int key0 = unit_key0(u);
+    const bool tail = key0 + kUnit > L;          // (wave-uniform) keys past L in this unit
+#pragma unroll
+    for (int i = 0; i < MqStage<TKV>::kChunks; ++i) {
+      const int ch = tid + kMqThreads * i;
+      const int key = ch / kKChunksPerRow, kc = ch % kKChunksPerRow;
+      bf16* kd = &sm.k[buf][(32 * (key >> 5) + krow(key & 31)) * kKRow + kEpc * kc];
+      const int d = ch / kVChunksPerRow, vc = ch % kVChunksPerRow;
+      bf16* vd = &sm.vt[buf][d * kVRow + kEpc * vc];
+      const int nvalid = L - (key0 + kEpc * vc);  // valid keys of this V^T chunk
+      if constexpr (kFp8) {
+        Frag8<bf16> lo, hi;
+        fp8x16_to_bf16(st.k[i], lo, hi);
+        lo.store(kd);
+        hi.store(kd + 8);
+        fp8x16_to_bf16(st.v[i], lo, hi);
+        if (tail) {
+          lo = lo.keep_first(nvalid);
+          hi = hi.keep_first(nvalid - 8);
+        }
+        lo.store(vd);
+        hi.store(vd + 8);
+      } else {
+        *reinterpret_cast<u32x4*>(kd) = st.k[i];
+        Frag8<bf16> f;
+        f.v = st.v[i];
+        if (tail) f = f.keep_first(nvalid);
+        f.store(vd);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBandPer; ++i) {
+      const int s = tid + kMqThreads * i;
+      if (s < G * kBandW) sm.band[buf][s] = to_f32(st.bias[i]) * kLog2e;
+    }
+  };
+
+  // ---- per-lane fragment offsets (elements).  S^T tile t of item ii: row r
+  // is key 32ii + 8(r/4) + 4t + r%4, so accumulator register r of lane group
+  // grp holds key 32ii + 8grp + 4t + r: each lane group ends up with 8
+  // consecutive keys, the B-operand layout of P^T.
+  int k_off[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) k_off[t] = krow(8 * (col >> 2) + (col & 3) + 4 * t) * kKRow + 8 * grp;
+  const int v_off = col * kVRow + 8 * grp;
+  const int band_off = hl * kBandW + token + (kUnit - 1) - 8 * grp;   // offset of key 8grp, ii = 0
+
+  float m = -INFINITY, l = 0.0f;                 // running max (log2 units), this lane's sum
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0, 0, 0, 0};
+
+  auto compute = [&](int u, int buf) {
+    if (!active) return;
+    const int key0 = unit_key0(u);
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sacc[ii][t] = f32x4{0, 0, 0, 0};
+        const bf16* kb = &sm.k[buf][32 * ii * kKRow + k_off[t]];
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds)
+          sacc[ii][t] = mfma16(Frag8<bf16>::load(kb + 32 * ds), qf[ds], sacc[ii][t]);
+      }
+    float x[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = key0 + 32 * ii + 8 * grp + e;
+        const bool ok = head_ok && j >= k_lo && j <= pos;
+        const float bv = sm.band[buf][band_off - 32 * ii - e];
+        x[8 * ii + e] = ok ? sacc[ii][e >> 2][e & 3] * c + bv : -INFINITY;
+        mx = fmaxf(mx, x[8 * ii + e]);
+      }
+    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = pair_max(mx);
+    const float m_new = fmaxf(m, mx);
+    const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = fast_exp2(m - m_sub);    // m = -inf -> 0
+    float p[16];
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = fast_exp2(x[e] - m_sub);
+      psum += p[e];
+    }
+    l = l * alpha + psum;
+    m = m_new;
+    Frag8<bf16> pf[2] = {Frag8<bf16>::pack(p), Frag8<bf16>::pack(p + 8)};
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      o[dt] *= alpha;
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+        o[dt] = mfma16(Frag8<bf16>::load(&sm.vt[buf][16 * dt * kVRow + v_off + 32 * ii]), pf[ii],
+                       o[dt]);
+    }
+  };
+
+  // ---- unit loop: unit u computes from LDS buffer u % 2 while units u+1
+  // (loaded, stored after the compute) and u+2 (issued before it) are in
+  // flight.  The two register sets alternate, so the loop is unrolled by two.
+  if (n_units > 0) {
+    MqStage<TKV> sa, sb;
+    stage_load(0, sa);
+    stage_load(1, sb);
+    stage_store(0, sa, 0);
+    lds_barrier();
+    for (int u = 0;; u += 2) {
+      stage_load(u + 2, sa);
+      compute(u, 0);
+      if (u + 1 >= n_units) break;
+      stage_store(u + 1, sb, 1);
+      lds_barrier();
+      stage_load(u + 3, sb);
+      compute(u + 1, 1);
+      if (u + 2 >= n_units) break;
+      stage_store(u + 2, sa, 0);
+      lds_barrier();
+    }
+  }
+
+  // ---- epilogue: O^T register r of dim tile dt is dim 16dt + 4grp + r.
+  if (!active) return;
+  float lt = l + wave_shfl_xor(l, 16);
+  lt = pair_sum(lt);
+  if (!head_ok) return;
+  const size_t orow = (size_t)(tok0 + token) * Hq + h;
+  const size_t prow = orow * S + split;
+  if (m == -INFINITY) {                          // no visible key in this split
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      store4(part_o + prow * kHeadDim + 16 * dt + 4 * grp, 0.0f, 0.0f, 0.0f, 0.0f);
+    if (grp == 0) part_lse[prow] = -INFINITY;
+    return;
+  }
+  const float sc = v_scale / lt;
+  const float row_lse = (m + fast_log2(lt)) * kLn2;
+  if (S == 1) {
+    // One split is the whole key range: the result goes straight out.
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      store4(out + orow * kHeadDim + 16 * dt + 4 * grp, o[dt][0] * sc, o[dt][1] * sc,
+             o[dt][2] * sc, o[dt][3] * sc);
+    if (lse != nullptr && grp == 0) lse[orow] = row_lse;
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      store4(part_o + prow * kHeadDim + 16 * dt + 4 * grp, o[dt][0] * sc, o[dt][1] * sc,
+             o[dt][2] * sc, o[dt][3] * sc);
+    if (grp == 0) part_lse[prow] = row_lse;
+  }
+}
+
+}  // namespace
+
+void launch_decode_mq_lds(const AttnShape& s, int num_seqs, int num_splits, const void* q,
+                          const void* k_cache, const void* v_cache, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                          const int32_t* seq_lens, const void* bias, void* out, float* lse,
+                          float* part_o, float* part_lse, const float* fp8_scales,
+                          hipStream_t stream) {
+  const unsigned groups = (unsigned)((long)num_splits * s.Hkv * num_seqs);
+  if (fp8_scales != nullptr)
+    hipLaunchKernelGGL(decode_mq_kernel<fp8e4>, dim3(groups), dim3(kMqThreads), 0, stream, s.Hq,
+                       s.Hkv, s.window, s.bias_len, num_splits, num_seqs, (const bf16*)q,
+                       (const fp8e4*)k_cache, (const fp8e4*)v_cache, block_table,
+                       max_blocks_per_seq, cu_seqlens_q, seq_lens, (const bf16*)bias, part_o,
+                       part_lse, (bf16*)out, lse, fp8_scales[0], fp8_scales[1]);
+  else
+    hipLaunchKernelGGL(decode_mq_kernel<bf16>, dim3(groups), dim3(kMqThreads), 0, stream, s.Hq,
+                       s.Hkv, s.window, s.bias_len, num_splits, num_seqs, (const bf16*)q,
+                       (const bf16*)k_cache, (const bf16*)v_cache, block_table,
+                       max_blocks_per_seq, cu_seqlens_q, seq_lens, (const bf16*)bias, part_o,
+                       part_lse, (bf16*)out, lse, 1.0f, 1.0f);
+}
+
+}  // namespace inkattn

@@ -48,6 +48,18 @@ hipError_t launch_prefill(const AttnShape& s, int num_seqs, int max_q_len, const
 // E4M3 cache (bf16 queries), or nullptr for a cache in the activation dtype.
 constexpr int decode_column_tiles(int G, int max_q_len) { return (G * max_q_len + 15) / 16; }
 
+// bf16 queries with 2 .. 8 column tiles run the LDS-staged multi-query kernel:
+// one work-group per (split, kv-head, sequence) holds every column.  Other
+// shapes run one work-group per (split, kv-head, sequence) and column group.
+constexpr bool decode_uses_lds_mq(int dtype, int G, int max_q_len) {
+  return dtype == kDtypeBf16 && decode_column_tiles(G, max_q_len) >= 2 &&
+         decode_column_tiles(G, max_q_len) <= 8;
+}
+// Work-groups per (split, kv-head, sequence).
+constexpr int decode_groups_per_pair(int dtype, int G, int max_q_len) {
+  return decode_uses_lds_mq(dtype, G, max_q_len) ? 1 : decode_column_tiles(G, max_q_len);
+}
+
 hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_tokens, int max_q_len,
                          int num_splits, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* block_table,
@@ -55,5 +67,14 @@ hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_tokens, int m
                          const int32_t* seq_lens, const void* bias, void* out, float* lse,
                          float* part_o, float* part_lse, const float* fp8_scales,
                          hipStream_t stream);
+
+// The LDS-staged multi-query split kernel alone (no merge); bf16 queries,
+// bf16 cache or (fp8_scales != nullptr) E4M3 cache.
+void launch_decode_mq_lds(const AttnShape& s, int num_seqs, int num_splits, const void* q,
+                          const void* k_cache, const void* v_cache, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                          const int32_t* seq_lens, const void* bias, void* out, float* lse,
+                          float* part_o, float* part_lse, const float* fp8_scales,
+                          hipStream_t stream);
 
 }  // namespace inkattn

@@ -202,9 +202,16 @@ def test_decode_mq_splits_and_workspace():
     # one token per sequence: the same heuristic as plain decode
     assert ink.inkattn_relattn_decode_mq_num_splits(d, 64, 1, 16384) == \
         ink.inkattn_relattn_decode_num_splits(d, 64, 16384)
-    # 9 tokens x 8 heads = 5 column tiles of 16: fewer splits fill the GPU
-    assert ink.inkattn_relattn_decode_mq_num_splits(d, 16, 9, 16384) == 1
-    assert ink.inkattn_relattn_decode_mq_num_splits(d, 2, 9, 16384) == 7
+    # bf16, 9 tokens x 8 heads = 5 column tiles of 16, all in one work-group
+    # per (split, kv-head, sequence): splits fill the 256 CUs once, capped by
+    # the 34 pages a 4096 + 8 key range can touch
+    assert ink.inkattn_relattn_decode_mq_num_splits(d, 16, 9, 16384) == 4
+    assert ink.inkattn_relattn_decode_mq_num_splits(d, 2, 9, 16384) == 32
+    assert ink.inkattn_relattn_decode_mq_num_splits(d, 1, 9, 16384) == 34
+    # fp32 keeps one work-group per column tile: 5 tiles, fewer splits
+    d32 = ink.make_desc(ink.FP32, 32, 4, 4096, 4096)
+    assert ink.inkattn_relattn_decode_mq_num_splits(d32, 16, 9, 16384) == 1
+    assert ink.inkattn_relattn_decode_mq_num_splits(d32, 2, 9, 16384) == 7
     n = ink.inkattn_relattn_decode_mq_workspace_size(d, 2, 10, 9, 16384, 3)
     rows = 10 * 32 * 3
     assert n == rows * 128 * 4 + ((rows * 4 + 15) // 16) * 16

@@ -14,11 +14,11 @@ from gpu_util import GpuCase, assert_close, assert_parity, host, oracle_kv, orac
 pytestmark = pytest.mark.gpu
 
 
-def _expected(case):
+def _expected(case, seqs=None):
     k_new, v_new, _ = oracle_sconv(case)
     G = case.num_q_heads // case.num_kv_heads
     outs, lses = [], []
-    for b in range(len(case.q_lens)):
+    for b in (range(len(case.q_lens)) if seqs is None else seqs):
         L, n = int(case.seq_lens[b]), int(case.q_lens[b])
         lo = max(0, L - n - case.window + 1) if case.window else 0
         K, V = oracle_kv(case, b, k_new, v_new, lo=lo)
@@ -29,14 +29,20 @@ def _expected(case):
     return np.concatenate(outs), np.concatenate(lses)
 
 
-def _run_and_check(case, num_splits=0):
+def _run_and_check(case, num_splits=0, seqs=None):
     gc = GpuCase(case)
     gc.sconv()
     out, lse = gc.decode_mq(num_splits)
     torch.cuda.synchronize()
-    want_o, want_l = _expected(case)
-    assert_parity(host(out), want_o, case.dtype, "out")
-    assert_parity(host(lse), want_l, case.dtype, "lse")
+    want_o, want_l = _expected(case, seqs)
+    if seqs is None:
+        got_o, got_l = host(out), host(lse)
+    else:
+        rows = np.concatenate([np.arange(case.cu_seqlens[b], case.cu_seqlens[b + 1])
+                               for b in seqs])
+        got_o, got_l = host(out)[rows], host(lse)[rows]
+    assert_parity(got_o, want_o, case.dtype, "out")
+    assert_parity(got_l, want_l, case.dtype, "lse")
     return gc, out, lse
 
 
@@ -57,6 +63,34 @@ def test_decode_mq_ragged(dtype, Hq, Hkv, W, R):
 def test_decode_mq_split_counts(num_splits):
     case = synth.make_case("fp32", [4, 9, 1], [2999, 5000, 640], 32, 4, 0, 6000, seed=41)
     _run_and_check(case, num_splits)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 5, 40])
+def test_decode_mq_split_counts_bf16(num_splits):
+    # 2, 5 and 1 column tiles in one call; splits that end mid-range and
+    # splits that own no page (40 > pages in range) go through the merge
+    case = synth.make_case("bf16", [4, 9, 1], [2999, 5000, 640], 32, 4, 0, 6000, seed=46)
+    _run_and_check(case, num_splits)
+
+
+def test_decode_mq_bf16_repeatable_across_calls():
+    case = synth.make_case("bf16", [9, 3, 7, 9], [4000, 127, 70, 9000], 32, 4, 2048, 2048,
+                           seed=47)
+    gc = GpuCase(case)
+    gc.sconv()
+    o1, l1 = gc.decode_mq(3)
+    o2, l2 = gc.decode_mq(3)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_mq_swa_16k_mtp9_sampled():
+    # the 16K sliding-window verification workload at full size (64 sequences
+    # x 9 query tokens, auto split count); the oracle checks every token and
+    # head of the first and the last sequence
+    wl = synth.WORKLOADS["swa_decode_16k_mtp9"]
+    case = synth.workload_case(wl, seed=0, past_device="cuda")
+    _run_and_check(case, seqs=[0, wl.batch - 1])
 
 
 def test_decode_mq_sixteen_tokens():
