@@ -16,8 +16,8 @@
 // byte of its range once:
 // * Units of 64 keys (half a page) go HBM -> registers -> LDS, every thread
 //   moving 16-byte chunks (coalesced: a wave load covers 1 KiB of a K page or
-//   eight 128-byte runs of its V^T rows).  Two units are in flight while a
-//   third is computed; one barrier per unit.  An E4M3 cache is converted to
+//   eight 128-byte runs of its V^T rows).  Three units are in flight while a
+//   fourth is computed; one barrier per unit.  An E4M3 cache is converted to
 //   bf16 on its way into LDS, so both caches share the compute below.
 // * Wave w owns column tile w (columns 16w .. 16w+15, token = column / G,
 //   head = column % G) and runs, per unit, S^T = K Q^T and O^T += V^T P^T on
@@ -51,11 +51,12 @@ constexpr int kMaxG = 16;                   // q-heads per kv-head
 constexpr int kBandW = 80;                  // >= 63 + 16 distances per head and unit
 constexpr int kBandSlots = kMaxG * kBandW;  // staged bias entries per unit
 constexpr int kBandPer = (kBandSlots + kMqThreads - 1) / kMqThreads;
+constexpr int kSets = 3;                    // units staged in registers / LDS buffers
 
 struct MqSmem {
-  bf16 k[2][kUnit * kKRow];                 // [key (permuted)][d]
-  bf16 vt[2][kHeadDim * kVRow];             // [d][key]
-  float band[2][kBandSlots];                // [head in group][distance - d_min]
+  bf16 k[kSets][kUnit * kKRow];             // [key (permuted)][d]
+  bf16 vt[kSets][kHeadDim * kVRow];         // [d][key]
+  float band[kSets][kBandSlots];            // [head in group][distance - d_min]
 };
 
 // LDS row, within its 32-key item, of key k (0 .. 31): bits 2 and 4 swapped.
@@ -77,6 +78,11 @@ template <typename TKV> struct MqStage {
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// Empty asms that consume a value: whatever computes it runs
+// unconditionally, and has completed, at this point.
+__device__ __forceinline__ void keep_live_f(float x) { asm volatile("" :: "v"(x)); }
+__device__ __forceinline__ void keep_live_frag(const Frag8<bf16>& f) { asm volatile("" :: "v"(f.v)); }
 
 // Sixteen E4M3 codes -> two bf16 fragments (elements 0-7 and 8-15), exactly.
 __device__ __forceinline__ void fp8x16_to_bf16(const u32x4& w, Frag8<bf16>& lo, Frag8<bf16>& hi) {
@@ -145,6 +151,10 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
     qf[ds] = head_ok ? Frag8<bf16>::load(q + ((size_t)(tok0 + token) * Hq + h) * kHeadDim +
                                          32 * ds + 8 * grp)
                      : Frag8<bf16>::zero();
+  // (waited for here, once: a wait inside the unit loop would also drain the
+  // K/V loads in flight)
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) keep_live_frag(qf[ds]);
 
   // ---- staging.  Unit u is page my_lo + u/2, keys 64(u%2) .. +63 of it.
   // Every load is unconditional (a unit index past the end re-reads the last
@@ -179,6 +189,10 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
       st.bias[i] = buf_load_elem<bf16>(
           bias_r, (uint32_t)(((kvh * G + e) * R + dist) * (int)sizeof(bf16)));
     }
+    // Keep a unit's loads together and in this order: the waits placed for
+    // a unit then count only the units issued after it (the scheduler would
+    // otherwise gather the bias loads of several units behind their K/V).
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto stage_store = [&](int u, const MqStage<TKV>& st, int buf) {
     const int key0 = unit_key0(u);
@@ -233,20 +247,40 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0, 0, 0, 0};
 
+  // Fragment reads are issued in batches of eight and consumed by an empty
+  // asm before their MFMAs, so each batch waits for LDS once rather than
+  // once per fragment.
   auto compute = [&](int u, int buf) {
     if (!active) return;
     const int key0 = unit_key0(u);
     f32x4 sacc[2][2];
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+    for (int ii = 0; ii < 2; ++ii) {
+      Frag8<bf16> kf[8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds)
+          kf[4 * t + ds] = Frag8<bf16>::load(&sm.k[buf][32 * ii * kKRow + k_off[t] + 32 * ds]);
+#pragma unroll
+      for (int f = 0; f < 8; ++f) keep_live_frag(kf[f]);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         sacc[ii][t] = f32x4{0, 0, 0, 0};
-        const bf16* kb = &sm.k[buf][32 * ii * kKRow + k_off[t]];
 #pragma unroll
-        for (int ds = 0; ds < 4; ++ds)
-          sacc[ii][t] = mfma16(Frag8<bf16>::load(kb + 32 * ds), qf[ds], sacc[ii][t]);
+        for (int ds = 0; ds < 4; ++ds) sacc[ii][t] = mfma16(kf[4 * t + ds], qf[ds], sacc[ii][t]);
       }
+    }
+    // Band entries are read for every key and consumed by an empty asm: left
+    // to itself the compiler reads only the visible ones, each behind a
+    // branch of its own.
+    float bv[16];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bv[8 * ii + e] = sm.band[buf][band_off - 32 * ii - e];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) keep_live_f(bv[e]);
     float x[16];
     float mx = -INFINITY;
 #pragma unroll
@@ -255,8 +289,7 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
       for (int e = 0; e < 8; ++e) {
         const int j = key0 + 32 * ii + 8 * grp + e;
         const bool ok = head_ok && j >= k_lo && j <= pos;
-        const float bv = sm.band[buf][band_off - 32 * ii - e];
-        x[8 * ii + e] = ok ? sacc[ii][e >> 2][e & 3] * c + bv : -INFINITY;
+        x[8 * ii + e] = ok ? sacc[ii][e >> 2][e & 3] * c + bv[8 * ii + e] : -INFINITY;
         mx = fmaxf(mx, x[8 * ii + e]);
       }
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
@@ -273,37 +306,50 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
     }
     l = l * alpha + psum;
     m = m_new;
-    Frag8<bf16> pf[2] = {Frag8<bf16>::pack(p), Frag8<bf16>::pack(p + 8)};
+    const Frag8<bf16> pf[2] = {Frag8<bf16>::pack(p), Frag8<bf16>::pack(p + 8)};
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      o[dt] *= alpha;
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii)
-        o[dt] = mfma16(Frag8<bf16>::load(&sm.vt[buf][16 * dt * kVRow + v_off + 32 * ii]), pf[ii],
-                       o[dt]);
+    for (int ii = 0; ii < 2; ++ii) {
+      Frag8<bf16> vf[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        vf[dt] = Frag8<bf16>::load(&sm.vt[buf][16 * dt * kVRow + v_off + 32 * ii]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) keep_live_frag(vf[dt]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] = mfma16(vf[dt], pf[ii], o[dt]);
     }
   };
 
-  // ---- unit loop: unit u computes from LDS buffer u % 2 while units u+1
-  // (loaded, stored after the compute) and u+2 (issued before it) are in
-  // flight.  The two register sets alternate, so the loop is unrolled by two.
+  // ---- unit loop: unit v sits in register set v % kSets until it is stored
+  // to LDS buffer v % kSets, right after the compute of unit v-1.  Unit v is
+  // computed while units v+1 and v+2 (issued two and one iterations earlier)
+  // and v+3 (issued just before) are in flight, so a unit's loads have two
+  // whole iterations to land.  The loop starts at v = -kSets so that the
+  // first units are loaded by the same code, into the same registers, as
+  // all later ones (a separate prologue made the compiler drain every load
+  // at the loop head); it is unrolled by kSets so that every register set
+  // and buffer index is static.
   if (n_units > 0) {
-    MqStage<TKV> sa, sb;
-    stage_load(0, sa);
-    stage_load(1, sb);
-    stage_store(0, sa, 0);
-    lds_barrier();
-    for (int u = 0;; u += 2) {
-      stage_load(u + 2, sa);
-      compute(u, 0);
-      if (u + 1 >= n_units) break;
-      stage_store(u + 1, sb, 1);
-      lds_barrier();
-      stage_load(u + 3, sb);
-      compute(u + 1, 1);
-      if (u + 2 >= n_units) break;
-      stage_store(u + 2, sa, 0);
-      lds_barrier();
+    MqStage<TKV> st[kSets];
+    for (int v0 = -kSets;; v0 += kSets) {
+      bool last = false;
+#pragma unroll
+      for (int r = 0; r < kSets; ++r) {
+        const int v = v0 + r;                      // v % kSets == r
+        stage_load(v + kSets, st[r]);              // set r was stored to LDS last iteration
+        if (v >= 0) compute(v, r);
+        if (v + 1 >= n_units) {
+          last = true;
+          break;
+        }
+        if (v + 1 >= 0) {
+          stage_store(v + 1, st[(r + 1) % kSets], (r + 1) % kSets);
+          lds_barrier();
+        }
+      }
+      if (last) break;
     }
   }
 
