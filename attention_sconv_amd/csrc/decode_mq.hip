@@ -19,10 +19,15 @@
 //   eight 128-byte runs of its V^T rows).  Three units are in flight while a
 //   fourth is computed; one barrier per unit.  An E4M3 cache is converted to
 //   bf16 on its way into LDS, so both caches share the compute below.
-// * Wave w owns column tile w (columns 16w .. 16w+15, token = column / G,
+// * Wave t owns column tile t (columns 16t .. 16t+15, token = column / G,
 //   head = column % G) and runs, per unit, S^T = K Q^T and O^T += V^T P^T on
 //   v_mfma_f32_16x16x32_bf16 with its fragments read from LDS, and the online
-//   softmax of its columns over the unit's 64 keys.
+//   softmax of its columns over the unit's two 32-key items.  Waves left over
+//   (8 - tiles) become partners of tiles 0, 1, ...: the owner then takes the
+//   first item of every unit and the partner the second, and the partner
+//   hands its (max, sum, O) to the owner through LDS at the end.  With 5
+//   tiles (9 tokens x 8 heads) the busiest SIMD runs 3 items per unit
+//   instead of 4.
 // * Sheared bias: the distances of a unit form, per head, a band of 63 + n
 //   entries; the band of every head of the group is staged with the unit
 //   (clamped at R - 1, pre-multiplied by log2 e) and read from LDS.
@@ -132,9 +137,15 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
   const int my_hi = min(my_lo + bps, blk_last + 1);
   const int n_units = 2 * max(my_hi - my_lo, 0);
 
-  // This wave's column tile (wave-uniform: whether it has one at all).
-  const bool active = 16 * wave < n_cols;
-  const int gc = 16 * wave + col;
+  // This wave's role (wave-uniform): its column tile and which items of
+  // every unit it computes (bit ii: item ii).
+  const int n_ct = (n_cols + 15) / 16;           // <= 8 (checked by the host)
+  const int n_pair = max(0, min(kMqWaves - n_ct, n_ct));
+  const bool partner = wave >= n_ct;
+  const int tile = partner ? wave - n_ct : wave;
+  const bool active = wave < n_ct + n_pair;
+  const int item_mask = tile >= n_pair ? 3 : (partner ? 2 : 1);
+  const int gc = 16 * tile + col;
   const bool head_ok = gc < n_cols;
   const int token = head_ok ? gc / G : 0;
   const int hl = head_ok ? gc % G : 0;           // head within the group
@@ -249,13 +260,16 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
 
   // Fragment reads are issued in batches of eight and consumed by an empty
   // asm before their MFMAs, so each batch waits for LDS once rather than
-  // once per fragment.
-  auto compute = [&](int u, int buf) {
-    if (!active) return;
+  // once per fragment.  kMask: the items of the unit this wave computes.
+  auto compute_items = [&](int u, int buf, auto mask_tag) {
+    constexpr int kMask = decltype(mask_tag)::value;
+    constexpr int kN = kMask == 3 ? 2 : 1;        // items
+    constexpr int kI0 = kMask == 2 ? 1 : 0;       // first item
     const int key0 = unit_key0(u);
-    f32x4 sacc[2][2];
+    f32x4 sacc[kN][2];
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
+    for (int n = 0; n < kN; ++n) {
+      const int ii = kI0 + n;
       Frag8<bf16> kf[8];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -266,51 +280,54 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
       for (int f = 0; f < 8; ++f) keep_live_frag(kf[f]);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        sacc[ii][t] = f32x4{0, 0, 0, 0};
+        sacc[n][t] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int ds = 0; ds < 4; ++ds) sacc[ii][t] = mfma16(kf[4 * t + ds], qf[ds], sacc[ii][t]);
+        for (int ds = 0; ds < 4; ++ds) sacc[n][t] = mfma16(kf[4 * t + ds], qf[ds], sacc[n][t]);
       }
     }
     // Band entries are read for every key and consumed by an empty asm: left
     // to itself the compiler reads only the visible ones, each behind a
     // branch of its own.
-    float bv[16];
+    float bv[8 * kN];
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+    for (int n = 0; n < kN; ++n)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bv[8 * ii + e] = sm.band[buf][band_off - 32 * ii - e];
+      for (int e = 0; e < 8; ++e) bv[8 * n + e] = sm.band[buf][band_off - 32 * (kI0 + n) - e];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) keep_live_f(bv[e]);
-    float x[16];
+    for (int e = 0; e < 8 * kN; ++e) keep_live_f(bv[e]);
+    float x[8 * kN];
     float mx = -INFINITY;
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+    for (int n = 0; n < kN; ++n)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int j = key0 + 32 * ii + 8 * grp + e;
+        const int j = key0 + 32 * (kI0 + n) + 8 * grp + e;
         const bool ok = head_ok && j >= k_lo && j <= pos;
-        x[8 * ii + e] = ok ? sacc[ii][e >> 2][e & 3] * c + bv[8 * ii + e] : -INFINITY;
-        mx = fmaxf(mx, x[8 * ii + e]);
+        x[8 * n + e] = ok ? sacc[n][e >> 2][e & 3] * c + bv[8 * n + e] : -INFINITY;
+        mx = fmaxf(mx, x[8 * n + e]);
       }
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
     mx = pair_max(mx);
     const float m_new = fmaxf(m, mx);
     const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
     const float alpha = fast_exp2(m - m_sub);    // m = -inf -> 0
-    float p[16];
+    float p[8 * kN];
     float psum = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 8 * kN; ++e) {
       p[e] = fast_exp2(x[e] - m_sub);
       psum += p[e];
     }
     l = l * alpha + psum;
     m = m_new;
-    const Frag8<bf16> pf[2] = {Frag8<bf16>::pack(p), Frag8<bf16>::pack(p + 8)};
+    Frag8<bf16> pf[kN];
+#pragma unroll
+    for (int n = 0; n < kN; ++n) pf[n] = Frag8<bf16>::pack(p + 8 * n);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
+    for (int n = 0; n < kN; ++n) {
+      const int ii = kI0 + n;
       Frag8<bf16> vf[8];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
@@ -318,8 +335,14 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) keep_live_frag(vf[dt]);
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] = mfma16(vf[dt], pf[ii], o[dt]);
+      for (int dt = 0; dt < 8; ++dt) o[dt] = mfma16(vf[dt], pf[n], o[dt]);
     }
+  };
+  auto compute = [&](int u, int buf) {
+    if (!active) return;
+    if (item_mask == 3) compute_items(u, buf, std::integral_constant<int, 3>{});
+    else if (item_mask == 1) compute_items(u, buf, std::integral_constant<int, 1>{});
+    else compute_items(u, buf, std::integral_constant<int, 2>{});
   };
 
   // ---- unit loop: unit v sits in register set v % kSets until it is stored
@@ -353,8 +376,42 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
     }
   }
 
+  // ---- partners hand (max, this lane's sum, O) to their owners: lane l of
+  // the owner holds the same (column, dims) as lane l of its partner.  The
+  // exchange reuses the K buffers once every wave is done with them.
+  if (n_pair > 0) {
+    constexpr int kX = 34;                       // floats per lane: m, l, 32 of O
+    float* xch = reinterpret_cast<float*>(&sm.k[0][0]);
+    static_assert(4 * kX * 64 * 4 <= (int)sizeof(sm.k), "exchange fits the K buffers");
+    lds_barrier();
+    if (active && partner) {
+      float* w = xch + tile * kX * 64 + lane;
+      w[0] = m;
+      w[64] = l;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[64 * (2 + 4 * dt + r)] = o[dt][r];
+    }
+    lds_barrier();
+    if (active && !partner && tile < n_pair) {
+      const float* w = xch + tile * kX * 64 + lane;
+      const float mp = w[0];
+      const float mt = fmaxf(m, mp);
+      if (mt != -INFINITY) {
+        const float a = fast_exp2(m - mt), bp = fast_exp2(mp - mt);
+        l = l * a + w[64] * bp;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[dt][r] = o[dt][r] * a + w[64 * (2 + 4 * dt + r)] * bp;
+        m = mt;
+      }
+    }
+  }
+
   // ---- epilogue: O^T register r of dim tile dt is dim 16dt + 4grp + r.
-  if (!active) return;
+  if (!active || partner) return;
   float lt = l + wave_shfl_xor(l, 16);
   lt = pair_sum(lt);
   if (!head_ok) return;
