@@ -451,8 +451,8 @@ def main():
             "frac": round(m_gbs / PEAK_HBM_GBS, 4),
             "tflops": round(4 * HEAD_DIM * m_pairs / (m_ms * 1e-3) / 1e12, 2),
             "time_vs_one_token_decode": round(m_ms / d_ms, 3),
-            "note": "inkattn_relattn_decode_mq; the 9 tokens of a sequence read its K/V once "
-                    "per 16 (token, head) columns",
+            "note": "inkattn_relattn_decode_mq; the 72 (token, head) columns of a kv-head "
+                    "group share one read of its K/V, staged through LDS",
         }
         del md
 

@@ -227,9 +227,11 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
  * seq_lens[b]-q_len .. seq_lens[b]-1, whose keys and values are already in
  * the cache (inkattn_sconv); each attends causally (and within the window)
  * with the logit of inkattn_relattn_prefill, so the result equals prefill
- * of those tokens with the sequence's earlier tokens as context.  K and V
- * are read once per (sequence, kv-head, split) for every 16 (token, q-head)
- * pairs of the group.
+ * of those tokens with the sequence's earlier tokens as context.  With bf16
+ * queries and 17 .. 128 (token, q-head) pairs per kv-head group, K and V are
+ * read once per (sequence, kv-head, split) for all of them (staged through
+ * LDS); otherwise once per 16 such pairs (fp32) or per 48 (bf16, larger
+ * groups).
  *   q    [num_tokens][Hq][128]        out [num_tokens][Hq][128]
  *   lse  float [num_tokens][Hq], or NULL
  *   cu_seqlens_q int32 [num_seqs+1], cu_seqlens_q[num_seqs] = num_tokens
