@@ -451,6 +451,10 @@ def main():
             "frac": round(m_gbs / PEAK_HBM_GBS, 4),
             "tflops": round(4 * HEAD_DIM * m_pairs / (m_ms * 1e-3) / 1e12, 2),
             "time_vs_one_token_decode": round(m_ms / d_ms, 3),
+            "traffic": recorded_traffic(
+                "decode_mq_bf16_swa_decode_16k_mtp9.traffic.txt",
+                ["attention_sconv_amd/csrc/decode_mq.hip",
+                 "attention_sconv_amd/csrc/device_common.h"]),
             "note": "inkattn_relattn_decode_mq; the 72 (token, head) columns of a kv-head "
                     "group share one read of its K/V, staged through LDS",
         }
