@@ -148,6 +148,25 @@ class DeviceCase:
                                            self.bias, self.out, None, 0, self.ws, self.ws_bytes)
 
 
+def recorded_field(profile, sources, field):
+    """Field `field` of profiles/<profile> (a rocprofv3 counter summary), or
+    None when the kernel's sources have changed since those counters were
+    taken (hash mismatch)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    try:
+        fields = dict(l.split(":", 1) for l in open(path).read().splitlines() if ":" in l)
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    recorded = fields.get("source_sha256_16", "").split()
+    if not recorded or recorded[0] != h.hexdigest()[:16] or field not in fields:
+        return None
+    return float(fields[field].split()[0])
+
+
 def recorded_traffic(profile, sources):
     """HBM bytes per launch recorded by the rocprofv3 FETCH_SIZE/WRITE_SIZE
     passes summarised in profiles/<profile>, or None when the kernel's
@@ -357,6 +376,10 @@ def main():
                          "prefill_bf16_swa_prefill_8k.traffic.txt",
                          ["attention_sconv_amd/csrc/prefill.hip",
                           "attention_sconv_amd/csrc/device_common.h"]),
+                     "mfma_busy_pct": recorded_field(
+                         "prefill_bf16_swa_prefill_8k.mfma.txt",
+                         ["attention_sconv_amd/csrc/prefill.hip",
+                          "attention_sconv_amd/csrc/device_common.h"], "mfma_busy_pct"),
                      "kernel": "prefill_kernel<bf16>", "ms": round(ms_prefill, 4),
                      "ms_median": round(float(np.median(ks)), 4),
                      "ms_min": round(min(ks), 4),
