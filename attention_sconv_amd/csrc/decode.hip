@@ -52,16 +52,25 @@ constexpr int kMaxTilesPerGroup = 3;
 // SIMD, so a wave may hold up to 512 registers) and keeps every tile's state
 // in the same wave, so each K/V fragment it loads serves all of its tiles.
 // Raw K/V registers of one item: the operand fragments themselves for a
-// cache in the activation type; for an E4M3 cache the codes, 8 per fragment
-// (K: this lane's 32 dims of its 2 keys, two 16-byte loads per key; V^T:
-// 8 tokens of one dim, one 8-byte load per dim tile), converted to bf16
-// fragments when the item is processed.
-template <typename T, typename TKV> struct ItemRegs {
+// cache in the activation type (32-key items); for an E4M3 cache the codes,
+// 8 per fragment, converted to bf16 fragments when the item is processed.
+// With several column tiles an E4M3 item has 32 keys (K: this lane's 32 dims
+// of its 2 keys, two 16-byte loads per key; V^T: 8 tokens of one dim, one
+// 8-byte load per dim tile).  With one column tile (kWide) it has 64 keys, so
+// that it carries the same 16 KB of K and V as a bf16 item and as many bytes
+// are in flight per prefetched item: K holds 4 keys per lane (two 16-byte
+// loads each), V^T 16 tokens of one dim per dim tile (one 16-byte load that
+// feeds both PV k-steps).
+template <typename T, typename TKV, bool kWide> struct ItemRegs {
   Frag8<T> k[8], v[8];
 };
-template <> struct ItemRegs<bf16, fp8e4> {
+template <> struct ItemRegs<bf16, fp8e4, false> {
   u32x4 k[4];
   u32x2 v[8];
+};
+template <> struct ItemRegs<bf16, fp8e4, true> {
+  u32x4 k[8];
+  u32x4 v[8];
 };
 
 // TKV: the cache element type, T or fp8e4 (bf16 queries only).  An E4M3 cache
@@ -117,7 +126,14 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
   const int bps = (nblk + S - 1) / S;
   const int my_lo = blk_first + split * bps;
   const int my_hi = min(my_lo + bps, blk_last + 1);
-  const int n_items = 4 * max(my_hi - my_lo, 0);   // item i: page my_lo + i/4, keys 32(i%4) ..
+  // Items: kIK keys each, 2^kIL per page.  Item i is page my_lo + i / 2^kIL,
+  // keys kIK (i % 2^kIL) .. of it; lane group G holds kKL consecutive keys.
+  constexpr bool kWide = kFp8 && kCT == 1;
+  constexpr int kIK = kWide ? 64 : 32;           // keys per item
+  constexpr int kIL = kWide ? 1 : 2;             // log2(items per page)
+  constexpr int kKL = kIK / 4;                   // keys per lane group
+  constexpr int kRT = kIK / 16;                  // S^T row tiles per item
+  const int n_items = (max(my_hi - my_lo, 0)) << kIL;
 
   // Per column tile u of this work-group: this lane's column, its query
   // position and visible keys k_lo .. pos, its bias row (an element index
@@ -158,9 +174,10 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
     const int phys = block_table[(size_t)b * max_blocks + blk];
     return ((size_t)phys * Hkv + kvh) * (size_t)(kPage * kHeadDim);
   };
-  // Row r of the S^T tile t of item (page, u) is key 32u + 8*(r/4) + 4t + r%4
-  // of the page, so accumulator register r of lane group G in tile t holds
-  // key 32u + 8G + 4t + r.
+  // Row r of the S^T tile t of item i is key kKL*(r/4) + 4t + r%4 of the
+  // item, so accumulator register r of lane group G in tile t holds key
+  // kKL*G + 4t + r: lane group G ends up with keys kKL*G .. kKL*G + kKL-1,
+  // the B-operand layout of P^T (8 keys per PV k-step).
   // Everything an item needs is loaded in one batch, one item ahead: K and
   // V^T fragments and, per column tile, the 8 bias entries of this lane's
   // keys.  Bias indices are clamped into the table (masked keys are dropped
@@ -171,23 +188,33 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
   // state is one fixed byte offset for K and one for V^T.
   constexpr uint32_t kPageBytes = kPage * kHeadDim * sizeof(TKV);
   const uint32_t k_lane =
-      ((8 * (col >> 2) + (col & 3)) * kHeadDim + (kFp8 ? 32 : 8) * grp) * sizeof(TKV);
-  const uint32_t v_lane = (col * kPage + 8 * grp) * sizeof(TKV);
-  using Regs = ItemRegs<T, TKV>;
-  auto load_item = [&](int item, Regs& ir, T (*bb)[8]) {
-    const int blk = my_lo + (item >> 2);
-    const int qu = item & 3;
-    const int j0 = blk * kPage + 32 * qu + 8 * grp;
+      ((kKL * (col >> 2) + (col & 3)) * kHeadDim + (kFp8 ? 32 : 8) * grp) * sizeof(TKV);
+  const uint32_t v_lane = (col * kPage + kKL * grp) * sizeof(TKV);
+  using Regs = ItemRegs<T, TKV, kWide>;
+  auto load_item = [&](int item, Regs& ir, T (*bb)[kKL]) {
+    const int blk = my_lo + (item >> kIL);
+    const int qu = item & ((1 << kIL) - 1);
+    const int j0 = blk * kPage + kIK * qu + kKL * grp;
 #pragma unroll
     for (int u = 0; u < kCT; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+      for (int e = 0; e < kKL; ++e)
         bb[u][e] = buf_load_elem<T>(
             bias_r, (bias_row[u] + min(max(pos[u] - (j0 + e), 0), R - 1)) * sizeof(T));
     const size_t base = page_base(blk);
     const rsrc_t kr = make_rsrc(k_cache + base, kPageBytes);
     const rsrc_t vr = make_rsrc(v_cache + base, kPageBytes);
-    if constexpr (kFp8) {
+    if constexpr (kWide) {
+#pragma unroll
+      for (int t = 0; t < kRT; ++t)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          ir.k[t * 2 + hh] = buf_load16(kr, k_lane + 4 * t * kHeadDim + 16 * hh,
+                                        kIK * qu * kHeadDim);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        ir.v[dt] = buf_load16(vr, v_lane, kIK * qu + 16 * dt * kPage);
+    } else if constexpr (kFp8) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -219,15 +246,79 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
     }
   };
   auto v_frag = [&](const Regs& ir, int dt) -> Frag8<T> {
-    if constexpr (kFp8) return fp8x8_to_bf16(ir.v[dt][0], ir.v[dt][1]);
+    if constexpr (kWide) return Frag8<T>::zero();   // (kWide items use v_frag_wide)
+    else if constexpr (kFp8) return fp8x8_to_bf16(ir.v[dt][0], ir.v[dt][1]);
     else return ir.v[dt];
+  };
+  // PV k-step s of a 64-key item: tokens kKL*G + 8s .. +7 of dim tile dt.
+  auto v_frag_wide = [&](const Regs& ir, int dt, int s) -> Frag8<T> {
+    if constexpr (kWide) return fp8x8_to_bf16(ir.v[dt][2 * s], ir.v[dt][2 * s + 1]);
+    else return Frag8<T>::zero();
+  };
+
+  // One 64-key E4M3 item, one column tile: scores, online softmax over the
+  // lane's 16 keys, O^T += V^T P^T in two k-steps.  The K and V fragments are
+  // converted right where the MFMAs consume them.
+  auto process_item_wide = [&](int item, Regs& ir, const T (*bb)[kKL]) {
+    const int blk = my_lo + (item >> kIL);
+    const int j0 = blk * kPage + kIK * (item & ((1 << kIL) - 1)) + kKL * grp;
+    f32x4 sacc[kRT];
+#pragma unroll
+    for (int t = 0; t < kRT; ++t) {
+      sacc[t] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) sacc[t] = mfma16(k_frag(ir, t, ds), qf[0][ds], sacc[t]);
+    }
+    float x[kKL];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kKL; ++e) {
+      const int j = j0 + e;
+      const bool ok = head_ok[0] && j >= k_lo[0] && j <= pos[0];
+      x[e] = ok ? sacc[e >> 2][e & 3] * c + to_f32(bb[0][e]) * kLog2e : -INFINITY;
+      mx = fmaxf(mx, x[e]);
+    }
+    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = pair_max(mx);
+    const float m_new = fmaxf(m[0], mx);
+    const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = fast_exp2(m[0] - m_sub);        // m = -inf -> 0
+    float p[kKL];
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kKL; ++e) {
+      p[e] = fast_exp2(x[e] - m_sub);
+      psum += p[e];
+    }
+    l[0] = l[0] * alpha + psum;
+    m[0] = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[0][dt] *= alpha;
+    // Keys >= L of the last page may hold any bits: zeroed in V (wave-uniform
+    // branch, per-lane select) so that 0 * garbage cannot reach O.
+    const bool tail = blk == blk_last && (L & (kPage - 1)) != 0;
+    const int nvalid = L - j0;
+#pragma unroll
+    for (int s = 0; s < kIK / 32; ++s) {
+      const Frag8<T> pf = Frag8<T>::pack(p + 8 * s);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        Frag8<T> vf = v_frag_wide(ir, dt, s);
+        if (tail) vf = vf.keep_first(nvalid - 8 * s);
+        o[0][dt] = mfma16(vf, pf, o[0][dt]);
+      }
+    }
   };
 
   // One item of 32 keys, for every column tile: scores, online softmax,
   // O^T += V^T P^T.
-  auto process_item = [&](int item, Regs& ir, const T (*bb)[8]) {
-    const int blk = my_lo + (item >> 2);
-    const int j0 = blk * kPage + 32 * (item & 3) + 8 * grp;
+  auto process_item = [&](int item, Regs& ir, const T (*bb)[kKL]) {
+    if constexpr (kWide) {
+      process_item_wide(item, ir, bb);
+      return;
+    }
+    const int blk = my_lo + (item >> kIL);
+    const int j0 = blk * kPage + kIK * (item & ((1 << kIL) - 1)) + kKL * grp;
     Frag8<T> kf[8], vf[8];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -297,7 +388,7 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
   // for a round that does not exist.  The barrier carries no memory fence:
   // it only holds waves together, it does not wait for their loads.
   Regs ra, rb;
-  T ba[kCT][8], bbb[kCT][8];
+  T ba[kCT][kKL], bbb[kCT][kKL];
   const int rounds = (n_items + kW - 1) / kW;
   auto item_of = [&](int r) { return min(r * kW + wave, n_items - 1); };
   auto has_item = [&](int r) { return r * kW + wave < n_items; };
