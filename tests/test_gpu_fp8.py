@@ -126,6 +126,16 @@ def test_decode_fp8_split_counts(num_splits):
     _run_and_check(case, (1 / 64, 1 / 64), num_splits)
 
 
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 40])
+def test_decode_fp8_one_token_split_counts(num_splits):
+    # one token per sequence and 8 heads per group: one column tile, 64-key
+    # items (a split's range can end on either half of a page); 40 splits
+    # leave splits of the shorter sequences without a page
+    case = synth.make_case("bf16", [1, 1, 1, 1], [2999, 5000, 640, 63], 32, 4, 0, 6000,
+                           seed=94)
+    _run_and_check(case, (1 / 64, 1 / 32), num_splits)
+
+
 def test_decode_fp8_equals_bf16_cache_of_the_same_values():
     # With power-of-two scales every read-back value is a bf16, so a bf16
     # cache can hold exactly the same keys and values: the two decodes differ
