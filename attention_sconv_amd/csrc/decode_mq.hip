@@ -57,6 +57,7 @@ constexpr int kBandW = 80;                  // >= 63 + 16 distances per head and
 constexpr int kBandSlots = kMaxG * kBandW;  // staged bias entries per unit
 constexpr int kBandPer = (kBandSlots + kMqThreads - 1) / kMqThreads;
 constexpr int kSets = 3;                    // units staged in registers / LDS buffers
+constexpr float kSlack = 8.0f;              // lazy-rescale threshold, log2 units
 
 struct MqSmem {
   bf16 k[kSets][kUnit * kKRow];             // [key (permuted)][d]
@@ -152,6 +153,17 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
   const int h = kvh * G + hl;
   const int pos = pos0 + token;
   const int k_lo = window > 0 ? max(0, pos - window + 1) : 0;
+  // Keys that every valid column of this wave sees: units inside
+  // [w_lo, w_hi] skip the per-key window mask (columns past n_cols then
+  // compute finite values nobody stores).
+  int w_lo = head_ok ? k_lo : 0, w_hi = head_ok ? pos : 0x7fffffff;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    w_lo = max(w_lo, __shfl_xor(w_lo, off, 64));
+    w_hi = min(w_hi, __shfl_xor(w_hi, off, 64));
+  }
+  w_lo = __builtin_amdgcn_readfirstlane(w_lo);
+  w_hi = __builtin_amdgcn_readfirstlane(w_hi);
   const float c = 0.08838834764831845f * kLog2e * k_scale;   // log2(e) / sqrt(128)
 
   // Q^T fragments (B operand): k-step ds of lane group grp holds dims
@@ -297,20 +309,39 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
     for (int e = 0; e < 8 * kN; ++e) keep_live_f(bv[e]);
     float x[8 * kN];
     float mx = -INFINITY;
+    const int j_first = key0 + 32 * kI0;         // this wave's keys: j_first .. j_first + 32kN - 1
+    if (j_first >= w_lo && j_first + 32 * kN - 1 <= w_hi) {
 #pragma unroll
-    for (int n = 0; n < kN; ++n)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = key0 + 32 * (kI0 + n) + 8 * grp + e;
-        const bool ok = head_ok && j >= k_lo && j <= pos;
-        x[8 * n + e] = ok ? sacc[n][e >> 2][e & 3] * c + bv[8 * n + e] : -INFINITY;
-        mx = fmaxf(mx, x[8 * n + e]);
+      for (int e = 0; e < 8 * kN; ++e) {
+        x[e] = sacc[e >> 3][(e >> 2) & 1][e & 3] * c + bv[e];
+        mx = fmaxf(mx, x[e]);
       }
+    } else {
+#pragma unroll
+      for (int n = 0; n < kN; ++n)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j_first + 32 * n + 8 * grp + e;
+          const bool ok = head_ok && j >= k_lo && j <= pos;
+          x[8 * n + e] = ok ? sacc[n][e >> 2][e & 3] * c + bv[8 * n + e] : -INFINITY;
+          mx = fmaxf(mx, x[8 * n + e]);
+        }
+    }
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
     mx = pair_max(mx);
-    const float m_new = fmaxf(m, mx);
-    const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = fast_exp2(m - m_sub);    // m = -inf -> 0
+    // Lazy rescale: the running max (and O with it) only moves when a
+    // column's max exceeds it by more than kSlack, so probabilities stay
+    // <= 2^kSlack; lanes that need no move keep alpha = 1 (and a column
+    // that has seen no key yet stays at -inf without -inf - -inf).
+    const bool need = mx > m + kSlack;
+    if (__any(need)) {
+      const float alpha = need ? fast_exp2(m - mx) : 1.0f;   // m = -inf -> 0
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+      m = need ? mx : m;
+    }
+    const float m_sub = m == -INFINITY ? 0.0f : m;
     float p[8 * kN];
     float psum = 0.0f;
 #pragma unroll
@@ -318,13 +349,10 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
       p[e] = fast_exp2(x[e] - m_sub);
       psum += p[e];
     }
-    l = l * alpha + psum;
-    m = m_new;
+    l += psum;
     Frag8<bf16> pf[kN];
 #pragma unroll
     for (int n = 0; n < kN; ++n) pf[n] = Frag8<bf16>::pack(p + 8 * n);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
 #pragma unroll
     for (int n = 0; n < kN; ++n) {
       const int ii = kI0 + n;
