@@ -9,6 +9,11 @@ the metric (split-K decode + LSE merge, after the one-token sconv) is measured
 in the same run on the 16K sliding-window decode workload (batch 64,
 L=16384, window 4096) and reported under "decode".
 
+The 32K full-causal prefill workload (batch 2, T=32768, Hq=32, Hkv=4, R=32768)
+is timed too, kernel alone, and reported under "prefill_32k"; so are the
+MTP9 verification step ("decode_mtp"), the 16K decode over an E4M3 cache
+("decode_fp8") and the sconv of a plain activation ("sconv_out").
+
 Prints ONE JSON line.  value = algorithmic attention FLOP per step / step
 time; roofline = the prefill kernel alone (HIP events on the launch stream).
 cpu_baseline = the fp64 oracle on a bounded sample of the same workload.
@@ -19,7 +24,7 @@ untimed steps bring the shader clock to its sustained level.  Decode is also
 timed with a 1 GiB streaming read before every step (L2 and MALL evicted).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--steady-s S]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--no-prefill-32k] [--no-decode]
 """
 
 import argparse
@@ -308,6 +313,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill-32k", action="store_true",
+                    help="skip the 32K full-causal prefill leg")
     ap.add_argument("--no-mtp", action="store_true",
                     help="skip the MTP-verification decode leg (it launches the decode kernel "
                          "with another shape)")
@@ -386,6 +393,39 @@ def main():
                      "algorithmic_flop": flop},
         "steady_clock_steps": n_steady,
     }
+
+    # ---------------- prefill on the 32K full-causal workload (kernel alone)
+    if not args.no_prefill_32k:
+        del dc
+        torch.cuda.empty_cache()
+        lwl = synth.WORKLOADS["full_prefill_32k"]
+        print(f"[bench] prefill {lwl.name}", file=sys.stderr, flush=True)
+        lcase = synth.workload_case(lwl, seed=0)
+        dc = DeviceCase(lcase, torch)
+        dc.sconv()
+        l_flop = 4 * HEAD_DIM * valid_pairs(lwl.q_len, lwl.seq_len, lwl.window) \
+            * lwl.num_q_heads * lwl.batch
+
+        def lstep(ev):
+            if ev is not None:
+                ev[0].record()
+            dc.prefill()
+            if ev is not None:
+                ev[1].record()
+
+        steady_clocks(torch, lstep, args.steady_s)
+        _, lks = time_region(torch, lstep, None, 5, 2)
+        l_ms = sum(lks) / len(lks)
+        l_tf = l_flop / (l_ms * 1e-3) / 1e12
+        result["prefill_32k"] = {
+            "workload": lwl.name + ": " + lwl.description + ", paged KV block 128",
+            "kernel": "prefill_kernel<bf16>", "ms": round(l_ms, 3),
+            "ms_median": round(float(np.median(lks)), 3), "algorithmic_flop": l_flop,
+            "achieved": round(l_tf, 1), "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
+            "frac": round(l_tf / PEAK_BF16_TFLOPS, 4),
+            "note": "prefill kernel alone (HIP events), 5 timed launches after 2 warmup",
+        }
+        del lcase
 
     # ---------------- decode: sconv (1 token/seq) + split-K decode, 16K SWA
     if not args.no_decode:
