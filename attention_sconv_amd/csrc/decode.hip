@@ -126,8 +126,12 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
   const int bps = (nblk + S - 1) / S;
   const int my_lo = blk_first + split * bps;
   const int my_hi = min(my_lo + bps, blk_last + 1);
-  // Items: kIK keys each, 2^kIL per page.  Item i is page my_lo + i / 2^kIL,
+  // Items: kIK keys each, 2^kIL per page.  Item i is page my_hi-1 - i / 2^kIL,
   // keys kIK (i % 2^kIL) .. of it; lane group G holds kKL consecutive keys.
+  // Pages are taken newest first: the page that the step's sconv has just
+  // written (lines partly dirty in the caches, slower to read) is then
+  // fetched while the rest of the range is still streaming, not at the end
+  // (a one-token step over 16K keys: 0.098 -> 0.096 ms after its sconv).
   constexpr bool kWide = kFp8 && kCT == 1;
   constexpr int kIK = kWide ? 64 : 32;           // keys per item
   constexpr int kIL = kWide ? 1 : 2;             // log2(items per page)
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
   const uint32_t v_lane = (col * kPage + kKL * grp) * sizeof(TKV);
   using Regs = ItemRegs<T, TKV, kWide>;
   auto load_item = [&](int item, Regs& ir, T (*bb)[kKL]) {
-    const int blk = my_lo + (item >> kIL);
+    const int blk = my_hi - 1 - (item >> kIL);
     const int qu = item & ((1 << kIL) - 1);
     const int j0 = blk * kPage + kIK * qu + kKL * grp;
 #pragma unroll
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
   // lane's 16 keys, O^T += V^T P^T in two k-steps.  The K and V fragments are
   // converted right where the MFMAs consume them.
   auto process_item_wide = [&](int item, Regs& ir, const T (*bb)[kKL]) {
-    const int blk = my_lo + (item >> kIL);
+    const int blk = my_hi - 1 - (item >> kIL);
     const int j0 = blk * kPage + kIK * (item & ((1 << kIL) - 1)) + kKL * grp;
     f32x4 sacc[kRT];
 #pragma unroll
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
       process_item_wide(item, ir, bb);
       return;
     }
-    const int blk = my_lo + (item >> kIL);
+    const int blk = my_hi - 1 - (item >> kIL);
     const int j0 = blk * kPage + kIK * (item & ((1 << kIL) - 1)) + kKL * grp;
     Frag8<T> kf[8], vf[8];
 #pragma unroll

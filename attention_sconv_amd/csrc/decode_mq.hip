@@ -179,15 +179,17 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
 #pragma unroll
   for (int ds = 0; ds < 4; ++ds) keep_live_frag(qf[ds]);
 
-  // ---- staging.  Unit u is page my_lo + u/2, keys 64(u%2) .. +63 of it.
+  // ---- staging.  Unit u is page my_hi-1 - u/2, keys 64(u%2) .. +63 of it.
   // Every load is unconditional (a unit index past the end re-reads the last
   // unit) so that each wait the compiler places covers exactly the loads it
   // needs and the next units stay in flight.
   const rsrc_t bias_r = make_rsrc(bias, (uint32_t)((size_t)Hq * R * sizeof(bf16)));
-  auto unit_key0 = [&](int u) { return (my_lo + (u >> 1)) * kPage + kUnit * (u & 1); };
+  // Pages are taken newest first (the page the step's sconv has just written
+  // is fetched early, while the rest of the range still streams).
+  auto unit_key0 = [&](int u) { return (my_hi - 1 - (u >> 1)) * kPage + kUnit * (u & 1); };
   auto stage_load = [&](int u, MqStage<TKV>& st) {
     u = min(u, n_units - 1);
-    const int blk = my_lo + (u >> 1);
+    const int blk = my_hi - 1 - (u >> 1);
     const int phys = block_table[(size_t)b * max_blocks + blk];
     const size_t base = ((size_t)phys * Hkv + kvh) * (size_t)(kPage * kHeadDim);
     const rsrc_t kr = make_rsrc(k_cache + base, kPageBytes);
