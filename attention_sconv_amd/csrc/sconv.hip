@@ -116,20 +116,19 @@ __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
   const int kvh = c0 / kHeadDim;
   const int dd = c0 % kHeadDim;
   // 8 outputs -> 8 cache elements at p (one 16-byte bf16 / 32-byte fp32
-  // store, or 8 E4M3 codes in one 8-byte store).  bf16 and E4M3 cache
-  // writes are nontemporal: a decode step writes one token per sequence, so
-  // its V^T stores are 2-byte pieces of many lines, and the decode right
-  // after it reads those lines faster when they do not sit partly dirty in
-  // the caches (16K SWA decode after its sconv: 0.096 -> 0.095 ms).
+  // store, or 8 E4M3 codes in one 8-byte store).  Single elements (the V^T
+  // column of a token that is not part of an aligned run of 8, as in a
+  // decode step) are stored nontemporally in bf16 and E4M3: they are 2-byte
+  // pieces of many lines, and the decode right after the step reads those
+  // lines faster when they do not sit partly dirty in the caches (16K SWA
+  // decode after its sconv: 0.096 -> 0.095 ms).  Whole 8-element stores stay
+  // ordinary: nontemporal, they slowed an 8K-token prefill write by 40%.
   const float inv = which ? inv_scale_v : inv_scale_k;
   auto store8 = [&](TC* p, const float* v8) {
     if constexpr (kFp8) {
-      __builtin_nontemporal_store(
+      *reinterpret_cast<u32x2*>(p) =
           u32x2{fp8x4_from_f32(v8[0] * inv, v8[1] * inv, v8[2] * inv, v8[3] * inv),
-                fp8x4_from_f32(v8[4] * inv, v8[5] * inv, v8[6] * inv, v8[7] * inv)},
-          reinterpret_cast<u32x2*>(p));
-    } else if constexpr (std::is_same<T, bf16>::value) {
-      __builtin_nontemporal_store(Frag8<T>::pack(v8).v, reinterpret_cast<u32x4*>(p));
+                fp8x4_from_f32(v8[4] * inv, v8[5] * inv, v8[6] * inv, v8[7] * inv)};
     } else {
       Frag8<T>::pack(v8).store(p);
     }
