@@ -7,9 +7,10 @@
                                  cache (a window-3 virtual layer; prefix caching);
 * ``inkattn_sconv_out``        -- the same convolution on a plain activation
                                  tensor (attention output, MoE output);
-* ``inkattn_sconv_fp8``, ``inkattn_relattn_decode_fp8`` -- the sconv cache
-                                 write and the (multi-query) decode with an
-                                 FP8 (OCP E4M3, scaled) KV cache;
+* ``inkattn_sconv_fp8``, ``inkattn_relattn_decode_fp8``,
+  ``inkattn_relattn_prefill_fp8`` -- the sconv cache write, the (multi-query)
+                                 decode and the prefill with an FP8 (OCP
+                                 E4M3, scaled) KV cache;
 * ``inkattn_relattn_prefill``  -- relative-position GQA attention over new
                                  tokens (bf16/fp32 MFMA, sheared bias band);
 * ``inkattn_relattn_decode``   -- split-K paged decode plus log-sum-exp merge;
@@ -32,6 +33,7 @@ from ._lib import (  # noqa: F401
     inkattn_sconv_paged, inkattn_sconv_out, inkattn_sconv_fp8, inkattn_relattn_decode_fp8,
     inkattn_relattn_decode_mq, inkattn_relattn_decode_mq_num_splits,
     inkattn_relattn_decode_mq_workspace_size,
+    inkattn_relattn_prefill_fp8, inkattn_relattn_prefill_fp8_workspace_size,
     inkattn_probe_mfma_bf16, inkattn_probe_stream_read,
     PROBE_MFMA_WAVES, PROBE_MFMA_CHAINS, PROBE_READ_GROUPS,
 )

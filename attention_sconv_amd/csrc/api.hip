@@ -222,6 +222,62 @@ inkattn_status_t inkattn_relattn_prefill(const inkattn_attn_desc_t* desc, int32_
                                           (hipStream_t)stream));
 }
 
+size_t inkattn_relattn_prefill_fp8_workspace_size(const inkattn_attn_desc_t* desc,
+                                                  int32_t num_seqs, int32_t max_blocks_per_seq) {
+  if (check_desc(desc) != INKATTN_OK || desc->dtype != INKATTN_BF16 || num_seqs < 0 ||
+      max_blocks_per_seq < 0)
+    return 0;
+  const size_t pages = (size_t)num_seqs * (size_t)max_blocks_per_seq;
+  const size_t page_bytes = (size_t)desc->num_kv_heads * 128 * 128 * 2;   // bf16
+  return 2 * pages * page_bytes + ((pages * 4 + 15) & ~(size_t)15);
+}
+
+inkattn_status_t inkattn_relattn_prefill_fp8(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                             int32_t num_tokens, int32_t max_q_len,
+                                             const void* q, const void* k_cache,
+                                             const void* v_cache, float k_scale, float v_scale,
+                                             const int32_t* block_table,
+                                             int32_t max_blocks_per_seq,
+                                             const int32_t* cu_seqlens_q,
+                                             const int32_t* seq_lens, const void* bias,
+                                             void* out, float* lse, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  inkattn_status_t st = check_desc(desc);
+  if (st != INKATTN_OK) return st;
+  if (desc->dtype != INKATTN_BF16) return INKATTN_ENOTSUP;
+  if (!fp8_scale_ok(k_scale) || !fp8_scale_ok(v_scale)) return INKATTN_EINVAL;
+  if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0) return INKATTN_EINVAL;
+  if (num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return INKATTN_OK;
+  if (max_blocks_per_seq < 1) return INKATTN_EINVAL;
+  if (!q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !seq_lens || !bias ||
+      !out || !workspace)
+    return INKATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(workspace))
+    return INKATTN_EINVAL;
+  if (bias_table_too_large(desc)) return INKATTN_ENOTSUP;
+  // Workspace pages are numbered with 32-bit block-table entries, and the
+  // conversion grid has one row per sequence.
+  const size_t pages = (size_t)num_seqs * (size_t)max_blocks_per_seq;
+  if (pages > 0x7fffffffULL || num_seqs > 65535) return INKATTN_ENOTSUP;
+  if (workspace_bytes < inkattn_relattn_prefill_fp8_workspace_size(desc, num_seqs,
+                                                                   max_blocks_per_seq))
+    return INKATTN_EINVAL;
+  const size_t page_bytes = (size_t)desc->num_kv_heads * 128 * 128 * 2;
+  char* ws = static_cast<char*>(workspace);
+  void* ws_k = ws;
+  void* ws_v = ws + pages * page_bytes;
+  int32_t* ws_table = reinterpret_cast<int32_t*>(ws + 2 * pages * page_bytes);
+  hipError_t e = inkattn::launch_fp8_pages_to_bf16(
+      desc->num_kv_heads, desc->window, num_seqs, max_blocks_per_seq, k_cache, v_cache,
+      block_table, cu_seqlens_q, seq_lens, ws_k, ws_v, ws_table, (hipStream_t)stream);
+  if (e != hipSuccess) return INKATTN_EHIP;
+  return from_hip(inkattn::launch_prefill(shape_of(desc), num_seqs, max_q_len, q, ws_k, ws_v,
+                                          ws_table, max_blocks_per_seq, cu_seqlens_q, seq_lens,
+                                          bias, out, lse, (hipStream_t)stream, k_scale,
+                                          v_scale));
+}
+
 int32_t inkattn_relattn_decode_num_splits(const inkattn_attn_desc_t* desc, int32_t num_seqs,
                                           int32_t max_seq_len) {
   if (check_desc(desc) != INKATTN_OK || num_seqs < 1 || max_seq_len < 1) return 1;

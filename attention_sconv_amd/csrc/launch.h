@@ -39,7 +39,17 @@ hipError_t launch_prefill(const AttnShape& s, int num_seqs, int max_q_len, const
                           const void* k_cache, const void* v_cache,
                           const int32_t* block_table, int max_blocks_per_seq,
                           const int32_t* cu_seqlens_q, const int32_t* seq_lens,
-                          const void* bias, void* out, float* lse, hipStream_t stream);
+                          const void* bias, void* out, float* lse, hipStream_t stream,
+                          float k_scale = 1.0f, float v_scale = 1.0f);
+
+// Pages of an E4M3 cache that the prefill of each sequence attends, as bf16
+// codes (exact) in a workspace cache: sequence b's block blk goes to
+// workspace page b * max_blocks + blk, which ws_table records.
+hipError_t launch_fp8_pages_to_bf16(int Hkv, int window, int num_seqs, int max_blocks,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                    const int32_t* seq_lens, void* ws_k, void* ws_v,
+                                    int32_t* ws_table, hipStream_t stream);
 
 // Decode over num_seqs sequences with 1 .. max_q_len query tokens each
 // (cu_seqlens_q == nullptr: exactly one token per sequence, token b of

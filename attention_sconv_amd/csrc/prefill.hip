@@ -100,6 +100,10 @@ struct PrefillArgs {
   void* out;
   float* lse;
   int Hq, Hkv, G, window, R, max_blocks, num_seqs, total_groups;
+  // Cache scales: the cache holds keys / k_scale and values / v_scale (1 and
+  // 1 for a cache of the values themselves; then every product below is
+  // exact and the results are those of the unscaled kernel, bit for bit).
+  float k_scale, v_scale;
 };
 
 // Row r of a 32-row S^T tile holds key keyperm(r): accumulator register j of
@@ -207,7 +211,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   Frag8<T> qf[8];
 
   const float sqrt_d = 11.313708498984761f;               // sqrt(128)
-  const float c = kLog2e / sqrt_d;
+  const float c = kLog2e / sqrt_d * A.k_scale;
+  const float band_mul = sqrt_d / A.k_scale;                // bias in units of the raw q.k
 
   // ---- staging.  Stage s holds K and the bias band of tile s and V of tile
   // s-1 (stage n_t holds only V of the last tile): V is consumed one tile
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
         const int dist = P0 - (jt_lo + x) * kBK + (kBQ - 1) - v;
         const bool vis = dist >= 0 && (A.window == 0 || dist < A.window);
         const float bv = dist > A.R - 1 ? bias_last : to_f32(raw[h * A.R + dist - e0]);
-        const float band_v = vis ? bv * sqrt_d : -INFINITY;
+        const float band_v = vis ? bv * band_mul : -INFINITY;
 #pragma unroll
         for (int sh = 0; sh < 4; ++sh)
           if (v - sh >= 0) sm.band[x & 1][sh][v - sh] = band_v;
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   // ---- epilogue: O^T register r of tile dt is dim 32dt + 8(r/4) + 4lg + r%4
   const float lt = pair_sum(l_sum);
   if (!row_ok) return;
-  const float inv = 1.0f / lt;
+  const float inv = A.v_scale / lt;
   T* op = static_cast<T*>(A.out) + ((size_t)(tok0 + row0 + a_row) * A.Hq + h) * kHeadDim;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -623,8 +628,10 @@ hipError_t launch_prefill(const AttnShape& s, int num_seqs, int max_q_len, const
                           const void* k_cache, const void* v_cache,
                           const int32_t* block_table, int max_blocks_per_seq,
                           const int32_t* cu_seqlens_q, const int32_t* seq_lens,
-                          const void* bias, void* out, float* lse, hipStream_t stream) {
+                          const void* bias, void* out, float* lse, hipStream_t stream,
+                          float k_scale, float v_scale) {
   PrefillArgs a;
+  a.k_scale = k_scale; a.v_scale = v_scale;
   a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table;
   a.cu_q = cu_seqlens_q; a.seq_lens = seq_lens; a.bias = bias; a.out = out; a.lse = lse;
   a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.Hq / s.Hkv; a.window = s.window; a.R = s.bias_len;

@@ -178,6 +178,36 @@ inkattn_status_t inkattn_relattn_prefill(const inkattn_attn_desc_t* desc, int32_
                                          const void* bias, void* out, float* lse,
                                          void* stream);
 
+/* Prefill over an E4M3 (OCP FP8) KV cache written by inkattn_sconv_fp8
+ * ([A] Roadmap: FP8 for the global-attention layers): the same logits and
+ * outputs as inkattn_relattn_prefill over a cache whose keys are
+ * code * k_scale and whose values are code * v_scale.  bf16 queries only.
+ * The blocks each sequence's chunk attends are first converted to bf16
+ * codes (exact) in `workspace`, which also holds a block table of its own;
+ * the prefill kernel then reads that copy and applies the scales.
+ *   k_cache, v_cache: uint8 codes, [num_blocks][Hkv][128][128] and
+ *                     [num_blocks][Hkv][128 dims][128 tokens].
+ *   workspace: device, 16-byte aligned, caller-owned scratch of at least
+ *              inkattn_relattn_prefill_fp8_workspace_size(...) bytes (two
+ *              bf16 page copies per (sequence, block) plus an int32 table);
+ *              its contents need no initialisation and are overwritten.
+ * Other arguments as inkattn_relattn_prefill.  INKATTN_ENOTSUP for an fp32
+ * desc, more than 65535 sequences or 2^31 (sequence, block) pages;
+ * INKATTN_EINVAL for a scale that is not positive and finite or a workspace
+ * that is too small. */
+size_t inkattn_relattn_prefill_fp8_workspace_size(const inkattn_attn_desc_t* desc,
+                                                  int32_t num_seqs, int32_t max_blocks_per_seq);
+inkattn_status_t inkattn_relattn_prefill_fp8(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                             int32_t num_tokens, int32_t max_q_len,
+                                             const void* q, const void* k_cache,
+                                             const void* v_cache, float k_scale, float v_scale,
+                                             const int32_t* block_table,
+                                             int32_t max_blocks_per_seq,
+                                             const int32_t* cu_seqlens_q,
+                                             const int32_t* seq_lens, const void* bias,
+                                             void* out, float* lse, void* workspace,
+                                             size_t workspace_bytes, void* stream);
+
 /* Number of KV splits inkattn_relattn_decode uses for num_splits = 0 (auto):
  * enough (sequence, kv-head, split) work-groups to fill the GPU, never more
  * splits than 128-token blocks in the attended range ([A] FA4 with sheared

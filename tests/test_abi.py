@@ -307,3 +307,38 @@ def test_decode_fp8_host_validation(kw, status):
 def test_decode_fp8_needs_bf16_queries():
     d = ink.make_desc(ink.FP32, 32, 4, 0, 128)
     assert _decode_fp8(d) == 2
+
+
+def _prefill_fp8(desc, **kw):
+    args = dict(num_seqs=2, num_tokens=5, max_q_len=4, q=FAKE, k=FAKE, v=FAKE, ks=0.5, vs=0.25,
+                bt=FAKE, mb=4, cu=FAKE, sl=FAKE, bias=FAKE, out=FAKE, lse=None, ws=FAKE,
+                ws_bytes=1 << 30)
+    args.update(kw)
+    return ink._lib._lib.inkattn_relattn_prefill_fp8(
+        ctypes.byref(desc), args["num_seqs"], args["num_tokens"], args["max_q_len"], args["q"],
+        args["k"], args["v"], args["ks"], args["vs"], args["bt"], args["mb"], args["cu"],
+        args["sl"], args["bias"], args["out"], args["lse"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_seqs=0), ink.OK), (dict(num_tokens=0), ink.OK), (dict(max_q_len=0), ink.OK),
+    (dict(ks=0.0), ink.EINVAL), (dict(vs=-1.0), ink.EINVAL), (dict(ks=float("inf")), ink.EINVAL),
+    (dict(ks=float("nan")), ink.EINVAL), (dict(ws=None), ink.EINVAL), (dict(ws=FAKE + 8), ink.EINVAL),
+    (dict(ws_bytes=1000), ink.EINVAL), (dict(mb=0), ink.EINVAL), (dict(q=None), ink.EINVAL),
+    (dict(num_seqs=70000, mb=1), ink.ENOTSUP),
+])
+def test_prefill_fp8_host_validation(kw, status):
+    d = ink.make_desc(ink.BF16, 32, 4, 0, 128)
+    assert _prefill_fp8(d, **kw) == status
+
+
+def test_prefill_fp8_rejects_fp32_and_sizes_workspace():
+    assert _prefill_fp8(ink.make_desc(ink.FP32, 32, 4, 0, 128)) == ink.ENOTSUP
+    d = ink.make_desc(ink.BF16, 32, 4, 2048, 2048)
+    # two bf16 copies of each (sequence, block) page (4 kv-heads x 128 x 128)
+    # plus an int32 block table, padded to 16 bytes
+    pages = 3 * 10
+    assert ink.inkattn_relattn_prefill_fp8_workspace_size(d, 3, 10) == \
+        2 * pages * 4 * 128 * 128 * 2 + (pages * 4 + 15) // 16 * 16
+    assert ink.inkattn_relattn_prefill_fp8_workspace_size(
+        ink.make_desc(ink.FP32, 32, 4, 0, 128), 3, 10) == 0

@@ -173,3 +173,46 @@ def test_decode_fp8_swa_16k_full_size():
     wl = synth.WORKLOADS["swa_decode_16k"]
     case = synth.workload_case(wl, seed=0, past_device="cuda")
     _run_and_check(case, (1 / 64, 1 / 64))
+
+
+def _run_prefill_and_check(case, scales):
+    gc = GpuCase(case, fp8_scales=scales)
+    gc.sconv()
+    out, lse = gc.prefill_fp8()
+    torch.cuda.synchronize()
+    want_o, want_l = _expected(case, gc)
+    assert_parity(host(out), want_o, "bf16", "out")
+    assert_parity(host(lse), want_l, "bf16", "lse")
+    return gc, out, lse
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (32, 4)])
+@pytest.mark.parametrize("W,R", [(0, 3000), (64, 64), (300, 40)])
+def test_prefill_fp8_chunks_after_context(Hq, Hkv, W, R):
+    # chunks of 1 .. 300 tokens after contexts that end on and off page edges
+    q_lens = [300, 1, 77, 129, 5]
+    ctx = [0, 127, 700, 256, 1500]
+    case = synth.make_case("bf16", q_lens, ctx, Hq, Hkv, W, R, seed=95 + Hq + W,
+                           extra_blocks=2)
+    _run_prefill_and_check(case, (1 / 64, 1 / 32))
+
+
+@pytest.mark.parametrize("scales", [(0.0173, 0.051), (2.0, 0.5)])
+def test_prefill_fp8_scales(scales):
+    case = synth.make_case("bf16", [200, 64], [900, 0], 32, 4, 512, 512, seed=96)
+    _run_prefill_and_check(case, scales)
+
+
+def test_prefill_fp8_matches_decode_fp8():
+    # the same query tokens through the E4M3 prefill and the E4M3 multi-query
+    # decode: two kernels, one definition
+    case = synth.make_case("bf16", [9, 3, 16], [4000, 127, 700], 32, 4, 2048, 2048, seed=97)
+    gc = GpuCase(case, fp8_scales=(1 / 64, 1 / 32))
+    gc.sconv()
+    op, lp = gc.prefill_fp8()
+    od, ld = gc.decode_fp8()
+    op2, lp2 = gc.prefill_fp8()
+    torch.cuda.synchronize()
+    assert torch.equal(op, op2) and torch.equal(lp, lp2)
+    assert_close(host(op), host(od), 2e-2, "prefill_fp8 vs decode_fp8")
+    assert_close(host(lp), host(ld), 2e-2, "lse prefill_fp8 vs decode_fp8")
