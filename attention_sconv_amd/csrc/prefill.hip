@@ -100,9 +100,8 @@ struct PrefillArgs {
   void* out;
   float* lse;
   int Hq, Hkv, G, window, R, max_blocks, num_seqs, total_groups;
-  // Cache scales: the cache holds keys / k_scale and values / v_scale (1 and
-  // 1 for a cache of the values themselves; then every product below is
-  // exact and the results are those of the unscaled kernel, bit for bit).
+  // Cache scales (read by the kScaled instance only): the cache holds
+  // keys / k_scale and values / v_scale.
   float k_scale, v_scale;
 };
 
@@ -160,7 +159,10 @@ template <> __device__ __forceinline__ u32x4 keep_first_elems<float>(u32x4 v, in
   return v;
 }
 
-template <typename T>
+// kScaled: apply the cache scales of A (a separate instance, so that the
+// kernel for a cache of the values themselves is compiled exactly without
+// them: the runtime factors cost that kernel ~3% through its schedule).
+template <typename T, bool kScaled>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   __shared__ PrefillSmem<T> sm;
 
@@ -211,8 +213,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   Frag8<T> qf[8];
 
   const float sqrt_d = 11.313708498984761f;               // sqrt(128)
-  const float c = kLog2e / sqrt_d * A.k_scale;
-  const float band_mul = sqrt_d / A.k_scale;                // bias in units of the raw q.k
+  const float c = kScaled ? kLog2e / sqrt_d * A.k_scale : kLog2e / sqrt_d;
+  const float band_mul = kScaled ? sqrt_d / A.k_scale : sqrt_d;   // bias in units of raw q.k
 
   // ---- staging.  Stage s holds K and the bias band of tile s and V of tile
   // s-1 (stage n_t holds only V of the last tile): V is consumed one tile
@@ -610,7 +612,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   // ---- epilogue: O^T register r of tile dt is dim 32dt + 8(r/4) + 4lg + r%4
   const float lt = pair_sum(l_sum);
   if (!row_ok) return;
-  const float inv = A.v_scale / lt;
+  const float inv = kScaled ? A.v_scale / lt : 1.0f / lt;
   T* op = static_cast<T*>(A.out) + ((size_t)(tok0 + row0 + a_row) * A.Hq + h) * kHeadDim;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -641,10 +643,16 @@ hipError_t launch_prefill(const AttnShape& s, int num_seqs, int max_q_len, const
   const long padded = ((long)a.total_groups + kXcds - 1) / kXcds * kXcds;
   const long blocks = padded * a.G;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  if (s.dtype == kDtypeBf16)
-    hipLaunchKernelGGL(prefill_kernel<bf16>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  const bool scaled = k_scale != 1.0f || v_scale != 1.0f;
+  if (s.dtype == kDtypeBf16 && scaled)
+    hipLaunchKernelGGL((prefill_kernel<bf16, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, a);
+  else if (s.dtype == kDtypeBf16)
+    hipLaunchKernelGGL((prefill_kernel<bf16, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<float, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

@@ -11,8 +11,9 @@ L=16384, window 4096) and reported under "decode".
 
 The 32K full-causal prefill workload (batch 2, T=32768, Hq=32, Hkv=4, R=32768)
 is timed too, kernel alone, and reported under "prefill_32k"; so are the
-MTP9 verification step ("decode_mtp"), the 16K decode over an E4M3 cache
-("decode_fp8") and the sconv of a plain activation ("sconv_out").
+MTP9 verification step ("decode_mtp"), the 8K prefill and the 16K decode over
+an E4M3 cache ("prefill_fp8", "decode_fp8") and the sconv of a plain activation
+("sconv_out").
 
 Prints ONE JSON line.  value = algorithmic attention FLOP per step / step
 time; roofline = the prefill kernel alone (HIP events on the launch stream).
@@ -143,6 +144,22 @@ class DeviceCase:
                                             self.block_table.shape[1], self.cu, self.seq_lens,
                                             self.bias, self.out, None, 0, self.ws,
                                             self.ws_bytes)
+
+    def setup_prefill_fp8(self, torch):
+        c = self.case
+        self.pf8_ws_bytes = self.ink.inkattn_relattn_prefill_fp8_workspace_size(
+            self.desc, len(c.q_lens), self.block_table.shape[1])
+        self.pf8_ws = torch.empty(self.pf8_ws_bytes // 4 + 4, dtype=torch.float32,
+                                  device="cuda")
+
+    def prefill_fp8(self):
+        c = self.case
+        self.ink.inkattn_relattn_prefill_fp8(self.desc, len(c.q_lens), c.num_tokens,
+                                             int(c.q_lens.max()), self.q, self.k_cache,
+                                             self.v_cache, self.fp8[0], self.fp8[1],
+                                             self.block_table, self.block_table.shape[1],
+                                             self.cu, self.seq_lens, self.bias, self.out, None,
+                                             self.pf8_ws, self.pf8_ws_bytes)
 
     def decode_mq(self):
         c = self.case
@@ -393,6 +410,35 @@ def main():
                      "algorithmic_flop": flop},
         "steady_clock_steps": n_steady,
     }
+
+    # ---------------- the 8K SWA prefill step over an E4M3 cache
+    if not args.no_fp8:
+        fcase8 = synth.workload_case(wl, seed=0)
+        fpd = DeviceCase(fcase8, torch, fp8_scales=(1 / 64, 1 / 64))
+        fpd.setup_prefill_fp8(torch)
+
+        def fpstep(ev):
+            fpd.sconv()
+            if ev is not None:
+                ev[0].record()
+            fpd.prefill_fp8()
+            if ev is not None:
+                ev[1].record()
+
+        print(f"[bench] prefill {wl.name} with an FP8 cache", file=sys.stderr, flush=True)
+        steady_clocks(torch, fpstep, args.steady_s)
+        _, fks = time_region(torch, fpstep, None, args.steps, args.warmup)
+        f_ms = sum(fks) / len(fks)
+        result["prefill_fp8"] = {
+            "workload": wl.name + " with an E4M3 KV cache (scales 1/64)",
+            "ms": round(f_ms, 4), "ms_median": round(float(np.median(fks)), 4),
+            "achieved": round(flop / (f_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "frac": round(flop / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "time_vs_bf16_cache": round(f_ms / ms_prefill, 3),
+            "note": "inkattn_relattn_prefill_fp8: page conversion to a bf16 workspace + "
+                    "prefill kernel, both inside the timed call",
+        }
+        del fpd, fcase8
 
     # ---------------- prefill on the 32K full-causal workload (kernel alone)
     if not args.no_prefill_32k:
