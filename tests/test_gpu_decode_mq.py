@@ -47,7 +47,7 @@ def _run_and_check(case, num_splits=0, seqs=None):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (32, 4), (16, 1)])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (32, 4), (16, 1), (8, 4)])
 @pytest.mark.parametrize("W,R", [(0, 5000), (64, 64), (300, 40)])
 def test_decode_mq_ragged(dtype, Hq, Hkv, W, R):
     # 1..9 query tokens (one accepted token and up to 8 drafts) on contexts
