@@ -216,3 +216,8 @@ def test_prefill_fp8_matches_decode_fp8():
     assert torch.equal(op, op2) and torch.equal(lp, lp2)
     assert_close(host(op), host(od), 2e-2, "prefill_fp8 vs decode_fp8")
     assert_close(host(lp), host(ld), 2e-2, "lse prefill_fp8 vs decode_fp8")
+
+
+def test_prefill_fp8_empty_chunks_in_batch():
+    case = synth.make_case("bf16", [0, 100, 0, 33], [50, 0, 300, 500], 32, 4, 64, 100, seed=99)
+    _run_prefill_and_check(case, (1 / 64, 1 / 32))

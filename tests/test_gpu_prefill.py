@@ -176,3 +176,15 @@ def test_prefill_window_and_table_edges(dtype, Hq, Hkv, W, R):
     case = synth.make_case(dtype, q_lens, ctx, Hq, Hkv, W, R, seed=70 + W % 97 + R % 13,
                            extra_blocks=1)
     _run_and_check(case, stored_kv=True)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_prefill_empty_chunks_in_batch(dtype):
+    # sequences with no new token in the batch: nothing of theirs is computed
+    # or written, and their sconv state stays as it was
+    case = synth.make_case(dtype, [0, 100, 0, 33], [50, 0, 300, 500], 32, 4, 64, 100, seed=98)
+    gc, out, lse = _run_and_check(case)
+    st = host(gc.conv_state)
+    for b in (0, 2):
+        slot = int(case.state_slot[b])
+        assert np.array_equal(st[slot], case.conv_state[slot])
