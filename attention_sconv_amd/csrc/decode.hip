@@ -10,9 +10,9 @@
 //
 // Split kernel: one work-group of 8 waves per (split, kv-head, sequence),
 // sized to fill one compute unit (2 waves per SIMD).  The split owns a
-// contiguous run of 128-token pages of the sequence's key range, cut into
-// items of 32 keys (page, quarter) dealt round-robin: in round r wave w
-// takes item 8r + w.  The SIMD arbiter favours the older of its two waves;
+// contiguous run of 128-token pages of the sequence's key range, newest page
+// first, cut into items of 32 keys (page, quarter; 64 keys, page and half,
+// for an E4M3 cache) dealt round-robin: in round r wave w takes item 8r + w.  The SIMD arbiter favours the older of its two waves;
 // left alone, the favoured waves would finish their share early and leave
 // the rest of the run at half occupancy, so the work-group meets at a
 // barrier every two rounds (no wave runs more than two items ahead, and the
@@ -314,8 +314,8 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
     }
   };
 
-  // One item of 32 keys, for every column tile: scores, online softmax,
-  // O^T += V^T P^T.
+  // One item (32 keys, or 64 for kWide), for every column tile: scores,
+  // online softmax, O^T += V^T P^T.
   auto process_item = [&](int item, Regs& ir, const T (*bb)[kKL]) {
     if constexpr (kWide) {
       process_item_wide(item, ir, bb);
