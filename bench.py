@@ -568,6 +568,33 @@ def main():
                     "group share one read of its K/V, staged through LDS",
         }
         del md
+        torch.cuda.empty_cache()
+        if not args.no_fp8:
+            # the same verification step over an E4M3 cache
+            mcase8 = synth.workload_case(mwl, seed=0, past_device="cuda")
+            mf = DeviceCase(mcase8, torch, fp8_scales=(1 / 64, 1 / 64))
+            mf.setup_decode_mq(torch)
+
+            def mfstep(ev):
+                mf.sconv()
+                if ev is not None:
+                    ev[0].record()
+                mf.decode_fp8()
+                if ev is not None:
+                    ev[1].record()
+
+            print(f"[bench] decode {mwl.name} with an FP8 cache", file=sys.stderr, flush=True)
+            steady_clocks(torch, mfstep, args.steady_s)
+            _, mfks = time_region(torch, mfstep, None, d_steps, args.warmup)
+            mf_ms = sum(mfks) / len(mfks)
+            result["decode_mtp"]["fp8_cache"] = {
+                "ms_decode": round(mf_ms, 4), "ms_decode_median": round(float(np.median(mfks)), 4),
+                "kv_bytes": m_kv_bytes // 2,
+                "achieved": round(m_kv_bytes / 2 / (mf_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                "speedup_vs_bf16_cache": round(m_ms / mf_ms, 3),
+                "note": "inkattn_relattn_decode_fp8 on the same workload (E4M3 codes, scales 1/64)",
+            }
+            del mf, mcase8
 
     # ---------------- FP8 (E4M3) KV cache: the 16K SWA decode step again
     if not args.no_decode and not args.no_fp8:
