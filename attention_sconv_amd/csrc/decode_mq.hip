@@ -30,11 +30,17 @@
 //   instead of 4.
 // * Sheared bias: the distances of a unit form, per head, a band of 63 + n
 //   entries; the band of every head of the group is staged with the unit
-//   (clamped at R - 1, pre-multiplied by log2 e) and read from LDS.
-// * K rows are stored in LDS with bits 2 and 4 of the key index swapped, so
-//   the 16 keys that a quarter-wave reads for one fragment sit in 16
-//   distinct bank groups (row stride 68 dwords); V^T rows (stride 36 dwords)
-//   are conflict-free as they are.
+//   (clamped at R - 1, pre-multiplied by log2 e) and read from LDS.  Head e's
+//   band starts 81 floats after head e-1's: with an even stride (80) the 64
+//   lanes of a band read fell on 8 bank offsets (a 4-way conflict at 8 heads
+//   per group, 8-way at 16); an odd one leaves at most 2 lanes per bank.
+// * K rows are stored in LDS with bits 2 and 4 of the key index swapped
+//   (row stride 68 dwords, V^T rows 36 dwords), so the 16 rows a quarter-wave
+//   reads for one fragment start in 16 distinct bank groups.  The LDS
+//   bank-conflict counter still reports conflict cycles for these reads
+//   (about 0.4 of the kernel's LDS-active cycles); rows of 72 / 40 dwords
+//   with an XOR of the lane-group chunk did not change it, so the counter's
+//   source there is not the address pattern modelled here.
 // Keys past the sequence end exist only in its last page and may hold any
 // bits: their V^T columns are zeroed on the way into LDS and their logits are
 // masked, so 0 * NaN never reaches O.
@@ -53,7 +59,8 @@ constexpr int kUnit = 64;                   // keys per staged unit (half a page
 constexpr int kKRow = kHeadDim + 8;         // LDS K row, elements (68 dwords)
 constexpr int kVRow = kUnit + 8;            // LDS V^T row, elements (36 dwords)
 constexpr int kMaxG = 16;                   // q-heads per kv-head
-constexpr int kBandW = 80;                  // >= 63 + 16 distances per head and unit
+constexpr int kBandW = 81;                  // >= 63 + 16 distances per head and unit; odd,
+                                            // so a band read's 64 lanes spread over the banks
 constexpr int kBandSlots = kMaxG * kBandW;  // staged bias entries per unit
 constexpr int kBandPer = (kBandSlots + kMqThreads - 1) / kMqThreads;
 constexpr int kSets = 3;                    // units staged in registers / LDS buffers
@@ -68,6 +75,14 @@ struct MqSmem {
 // LDS row, within its 32-key item, of key k (0 .. 31): bits 2 and 4 swapped.
 __device__ __forceinline__ int krow(int k) {
   return (k & 0x0b) | ((k & 0x04) << 2) | ((k & 0x10) >> 2);
+}
+
+// Max over the lane pair (l, l ^ 16) with v_permlane16_swap (a VALU op, no
+// LDS round trip): after the swap the two result registers hold lane l's
+// value and its partner's.
+__device__ __forceinline__ float row_pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // A unit's raw chunks in flight: 16-byte chunks of K and of V^T per thread
@@ -329,7 +344,7 @@ __global__ __launch_bounds__(kMqThreads) void decode_mq_kernel(
           mx = fmaxf(mx, x[8 * n + e]);
         }
     }
-    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = row_pair_max(mx);
     mx = pair_max(mx);
     // Lazy rescale: the running max (and O with it) only moves when a
     // column's max exceeds it by more than kSlack, so probabilities stay
