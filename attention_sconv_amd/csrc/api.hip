@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "launch.h"
@@ -13,9 +14,27 @@ using inkattn::AttnShape;
 
 namespace {
 
-constexpr int kCUs = 256;                  // MI355X compute units
-constexpr int kDecodeTargetGroups = kCUs;   // (seq, kv-head, split) work-groups, one per CU
+constexpr int kDefaultCUs = 256;            // MI355X, when no device answers the query
 constexpr int kMaxDecodeQueries = 16;       // query tokens per sequence in one decode call
+
+// Compute units of the current device: the split heuristic aims at about one
+// (sequence, kv-head, split) work-group per CU.  Read once per device.
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kDefaultCUs;
+  if (dev < kMaxDevices) {
+    const int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n < 1)
+    n = kDefaultCUs;
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 // A cache scale must be positive and finite, with a finite reciprocal.
@@ -57,7 +76,8 @@ int32_t auto_splits(const inkattn_attn_desc_t* d, int32_t num_seqs, int32_t max_
                                                         max_q_len);
   const int64_t nblk = blocks_in_range(d, max_seq_len, max_q_len);
   if (pairs <= 0 || nblk <= 0) return 1;
-  int64_t s = (kDecodeTargetGroups + pairs - 1) / pairs;
+  const int64_t target = device_cus();
+  int64_t s = (target + pairs - 1) / pairs;
   if (s > nblk) s = nblk;
   if (s < 1) s = 1;
   return (int32_t)s;
@@ -70,11 +90,13 @@ bool bias_table_too_large(const inkattn_attn_desc_t* d) {
 }
 
 // The decode grid is one dimension of (split, kv-head, sequence) x column
-// tile work-groups, with 32-bit indices inside the kernel.
-bool decode_grid_too_large(const inkattn_attn_desc_t* d, int64_t num_seqs, int64_t splits,
-                           int32_t max_q_len) {
+// tile work-groups, with 32-bit indices inside the kernel; the merge grid is
+// one dimension of (query token, q-head) work-groups.
+bool decode_grid_too_large(const inkattn_attn_desc_t* d, int64_t num_seqs, int64_t num_tokens,
+                           int64_t splits, int32_t max_q_len) {
   const int64_t rest = splits * d->num_kv_heads * num_seqs;
   const int64_t n_ct = inkattn::decode_column_tiles(d->num_q_heads / d->num_kv_heads, max_q_len);
+  if ((int64_t)d->num_q_heads * num_tokens > 0x7fffffffLL) return true;
   return (rest + 7) / 8 * 8 * n_ct > 0x7fffffffLL;   // (covers the LDS-staged grid, rest)
 }
 
@@ -314,7 +336,7 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
     return INKATTN_EINVAL;
   if (bias_table_too_large(desc)) return INKATTN_ENOTSUP;
   const int32_t s = num_splits == 0 ? auto_splits(desc, num_seqs, max_seq_len) : num_splits;
-  if (decode_grid_too_large(desc, num_seqs, s, 1)) return INKATTN_ENOTSUP;
+  if (decode_grid_too_large(desc, num_seqs, num_seqs, s, 1)) return INKATTN_ENOTSUP;
   const size_t need = inkattn_relattn_decode_workspace_size(desc, num_seqs, max_seq_len, s);
   if (workspace_bytes < need) return INKATTN_EINVAL;
   const size_t rows = (size_t)num_seqs * desc->num_q_heads * (size_t)s;
@@ -379,7 +401,7 @@ static inkattn_status_t decode_mq_common(const inkattn_attn_desc_t* desc, int32_
   if (bias_table_too_large(desc)) return INKATTN_ENOTSUP;
   const int32_t s =
       num_splits == 0 ? auto_splits(desc, num_seqs, max_seq_len, max_q_len) : num_splits;
-  if (decode_grid_too_large(desc, num_seqs, s, max_q_len)) return INKATTN_ENOTSUP;
+  if (decode_grid_too_large(desc, num_seqs, num_tokens, s, max_q_len)) return INKATTN_ENOTSUP;
   const size_t need = inkattn_relattn_decode_mq_workspace_size(desc, num_seqs, num_tokens,
                                                                max_q_len, max_seq_len, s);
   if (workspace_bytes < need) return INKATTN_EINVAL;

@@ -471,8 +471,10 @@ template <typename T>
 __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(
     int Hq, int S, const float* __restrict__ part_o, const float* __restrict__ part_lse,
     T* __restrict__ out, float* __restrict__ lse) {
-  const int h = blockIdx.x;
-  const int t = blockIdx.y;                      // query token
+  // one work-group per (query token, q-head) on a 1-D grid (token counts
+  // beyond the 65535 a grid's y dimension holds)
+  const int h = blockIdx.x % Hq;
+  const int t = blockIdx.x / Hq;                 // query token
   const int d = threadIdx.x;
   const size_t row0 = ((size_t)t * Hq + h) * S;
   float M = -INFINITY;
@@ -511,7 +513,8 @@ void launch_split(const AttnShape& s, int num_seqs, int num_splits, int n_cg, co
 template <typename T>
 void launch_merge(const AttnShape& s, int num_tokens, int num_splits, float* part_o,
                   float* part_lse, void* out, float* lse, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_merge_kernel<T>, dim3(s.Hq, num_tokens), dim3(kHeadDim), 0, stream,
+  hipLaunchKernelGGL(decode_merge_kernel<T>, dim3((unsigned)((long)s.Hq * num_tokens)),
+                     dim3(kHeadDim), 0, stream,
                      s.Hq, num_splits, part_o, part_lse, (T*)out, lse);
 }
 

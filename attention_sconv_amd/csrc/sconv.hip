@@ -35,6 +35,11 @@ namespace inkattn {
 
 constexpr int kSconvTok = 8;          // tokens per thread
 constexpr int kSconvRows = 4;         // token chunks per work-group (blockDim.y)
+// At most 256 threads per work-group: a thread holds 11 rows of 8 channels
+// and 64 fp32 outputs, which needs more than the 128 VGPRs a 1024-thread
+// bound leaves (that bound made the kernels spill).  Channels beyond 256
+// threads' worth go to further work-groups along grid z.
+constexpr int kSconvThreads = 256;
 
 // Paged-state arguments (unused by the dense-state kernel).
 struct SconvPaged {
@@ -48,20 +53,21 @@ struct SconvPaged {
 // FP8 cache (TC = fp8e4): the outputs are stored as E4M3 codes of y / scale;
 // inv_scale[0|1] = 1 / scale of the key | value cache.
 template <typename T, typename TC, bool kPaged>
-__global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
+__global__ __launch_bounds__(kSconvThreads) void sconv_cache_write_kernel(
     int C, int Hkv, const T* __restrict__ k_in, const T* __restrict__ v_in,
     const T* __restrict__ conv_w, T* __restrict__ conv_state,
     const int32_t* __restrict__ state_slot, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ slot_mapping, TC* __restrict__ k_cache,
     TC* __restrict__ v_cache, SconvPaged pg, float inv_scale_k, float inv_scale_v) {
   constexpr bool kFp8 = std::is_same<TC, fp8e4>::value;
-  const int which = blockIdx.z;              // 0 = keys, 1 = values
+  const int ncg = gridDim.z >> 1;            // channel groups
+  const int which = blockIdx.z / ncg;        // 0 = keys, 1 = values
   const int b = blockIdx.y;
   const int r0 = (blockIdx.x * blockDim.y + threadIdx.y) * kSconvTok;   // first token (relative)
-  const int c0 = threadIdx.x * 8;
+  const int c0 = ((blockIdx.z % ncg) * blockDim.x + threadIdx.x) * 8;
   const int t_begin = cu_seqlens[b];
   const int n = cu_seqlens[b + 1] - t_begin;
-  if (r0 >= n) return;
+  if (r0 >= n || c0 >= C) return;
 
   const T* x = (which ? v_in : k_in) + (size_t)t_begin * C + c0;
   const T* wp = conv_w + ((size_t)which * C + c0) * 4;
@@ -207,16 +213,16 @@ __global__ __launch_bounds__(1024) void sconv_cache_write_kernel(
 // the dense three-token state [slots][3][C].  Same work split as above: each
 // thread owns 8 channels and kSconvTok tokens of one sequence.
 template <typename T>
-__global__ __launch_bounds__(1024) void sconv_out_kernel(
+__global__ __launch_bounds__(kSconvThreads) void sconv_out_kernel(
     int C, const T* __restrict__ x_in, const T* __restrict__ conv_w, T* __restrict__ conv_state,
     const int32_t* __restrict__ state_slot, const int32_t* __restrict__ cu_seqlens,
     T* __restrict__ y_out) {
   const int b = blockIdx.y;
   const int r0 = (blockIdx.x * blockDim.y + threadIdx.y) * kSconvTok;   // first token (relative)
-  const int c0 = threadIdx.x * 8;
+  const int c0 = (blockIdx.z * blockDim.x + threadIdx.x) * 8;
   const int t_begin = cu_seqlens[b];
   const int n = cu_seqlens[b + 1] - t_begin;
-  if (r0 >= n) return;
+  if (r0 >= n || c0 >= C) return;
   const T* x = x_in + (size_t)t_begin * C + c0;
   T* y = y_out + (size_t)t_begin * C + c0;
   T* st = conv_state + (size_t)state_slot[b] * 3 * C + c0;
@@ -268,9 +274,10 @@ __global__ __launch_bounds__(1024) void sconv_out_kernel(
 hipError_t launch_sconv_out(int dtype, int C, int num_seqs, int max_chunk_len, const void* x,
                             const void* conv_w, void* conv_state, const int32_t* state_slot,
                             const int32_t* cu_seqlens, void* y, hipStream_t stream) {
-  dim3 block(C / 8, 1);
-  block.y = (unsigned)max(1, min(kSconvRows, 1024 / (C / 8)));
-  dim3 grid((max_chunk_len + kSconvTok * block.y - 1) / (kSconvTok * block.y), num_seqs, 1);
+  dim3 block(min(C / 8, kSconvThreads), 1);
+  block.y = (unsigned)max(1, min(kSconvRows, kSconvThreads / (int)block.x));
+  dim3 grid((max_chunk_len + kSconvTok * block.y - 1) / (kSconvTok * block.y), num_seqs,
+            (C / 8 + block.x - 1) / block.x);
   if (dtype == kDtypeBf16)
     hipLaunchKernelGGL(sconv_out_kernel<bf16>, grid, block, 0, stream, C, (const bf16*)x,
                        (const bf16*)conv_w, (bf16*)conv_state, state_slot, cu_seqlens, (bf16*)y);
@@ -289,13 +296,11 @@ hipError_t launch_sconv_any(int dtype, int Hkv, int num_seqs, int max_chunk_len,
                             void* k_cache, void* v_cache, const SconvPaged& pg,
                             const float* fp8_scales, hipStream_t stream) {
   const int C = Hkv * kHeadDim;
-  const int per_block = kSconvTok * kSconvRows;
-  dim3 grid((max_chunk_len + per_block - 1) / per_block, num_seqs, 2);
-  dim3 block(C / 8, kSconvRows);
-  if (block.x * block.y > 1024) {                            // Hkv > 16
-    block.y = 1024 / block.x;
-    grid.x = (max_chunk_len + kSconvTok * block.y - 1) / (kSconvTok * block.y);
-  }
+  dim3 block(min(C / 8, kSconvThreads), 1);
+  block.y = (unsigned)max(1, min(kSconvRows, kSconvThreads / (int)block.x));
+  const int ncg = (C / 8 + block.x - 1) / block.x;           // channel groups (Hkv > 16)
+  dim3 grid((max_chunk_len + kSconvTok * block.y - 1) / (kSconvTok * block.y), num_seqs,
+            2 * ncg);
   auto go = [&](auto t_tag, auto c_tag) {
     using T = decltype(t_tag);
     using TC = decltype(c_tag);

@@ -3,29 +3,36 @@
 One step = one pass of the hot path over one batch of synthetic input:
   inkattn_sconv            (K/V short convolution + paged KV-cache write)
   inkattn_relattn_prefill  (relative-position GQA attention over the chunk)
-on the sliding-window prefill workload (batch 1, T=8192, Hq=32, Hkv=4,
-d=128, window 2048, R=2048, bf16, paged KV block 128).  The decode half of
-the metric (split-K decode + LSE merge, after the one-token sconv) is measured
-in the same run on the 16K sliding-window decode workload (batch 64,
-L=16384, window 4096) and reported under "decode".
+on the full-causal prefill workload (batch 2, T=32768, Hq=32, Hkv=4, d=128,
+R=32768, bf16, paged KV block 128), the largest workload that fits one GPU.
+value = its attention FLOP per step / step time; roofline = the prefill
+kernel alone (HIP events on its launch stream); sconv = the K/V sconv and
+cache write alone, in GB/s.
 
-The 32K full-causal prefill workload (batch 2, T=32768, Hq=32, Hkv=4, R=32768)
-is timed too, kernel alone, and reported under "prefill_32k"; so are the
-MTP9 verification step ("decode_mtp"), the 8K prefill and the 16K decode over
-an E4M3 cache ("prefill_fp8", "decode_fp8") and the sconv of a plain activation
-("sconv_out").
-
-Prints ONE JSON line.  value = algorithmic attention FLOP per step / step
-time; roofline = the prefill kernel alone (HIP events on the launch stream).
-cpu_baseline = the fp64 oracle on a bounded sample of the same workload.
-ceilings = a dense bf16 MFMA loop (with the shader clock it ran at) and a
-4 GiB streaming read, measured in the same job; frac_of_measured divides by
-them.  Before the warmup steps of each leg, about --steady-s seconds of
-untimed steps bring the shader clock to its sustained level.  Decode is also
-timed with a 1 GiB streaming read before every step (L2 and MALL evicted).
+Further legs in the same JSON line:
+  prefill_8k     the 8K sliding-window prefill step (T=8192, window 2048)
+  prefill_fp8    the same over an E4M3 KV cache
+  decode         16K sliding-window decode (64 sequences, window 4096):
+                 one-token sconv + split-K decode (+ merge when split)
+  decode_1m      1M-context full-attention decode (4 sequences): split-K
+                 pass + LSE merge, timed together; decode_1m_fp8 over E4M3
+  decode_mtp     MTP verification: 9 query tokens per sequence, 16K window
+  decode_fp8     the 16K decode over an E4M3 cache
+  sconv_out      the sconv of a plain [tokens][channels] activation
+  ceilings       a dense bf16 MFMA loop (with its shader clock) and a 4 GiB
+                 streaming read, measured in the same job
+  cpu_baseline   the fp64 oracle on the host cores: the headline workload on
+                 a stratified sample (extrapolated by pair count), the tiny
+                 and 8K prefill in full, the 16K and 1M decode on some of
+                 their sequences
+Decode legs are also timed with a 1 GiB streaming read before every step
+(L2 and MALL evicted).  Before the warmup steps of each leg, about
+--steady-s seconds of untimed steps bring the shader clock to its sustained
+level.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--steady-s S]
-                       [--no-cpu-baseline] [--no-prefill-32k] [--no-decode]
+                       [--no-cpu-baseline] [--no-prefill-8k] [--no-decode]
+                       [--no-1m] [--no-mtp] [--no-fp8] [--no-sconv-out]
 """
 
 import argparse
@@ -286,76 +293,177 @@ def ceilings(torch, ink):
                     "256 threads x 8 loads of 16 B in flight), same job"}
 
 
-def cpu_baseline(case, budget_s=10.0):
-    """The fp64 oracle on the prefill workload, timed on the host cores: the
-    sconv of the chunk, then attention of all query rows (all heads) in
-    blocks of 256, repeated until at least ``budget_s`` seconds of work."""
-    import oracle
+# ---------------------------------------------------------------- CPU baseline
+def _cores():
+    """Host cores: os.cpu_count(), the affinity set, and the BLAS threads the
+    oracle's matrix products run on (its elementwise numpy work is one
+    thread)."""
+    nproc = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = nproc
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        cores = 1
+        blas = 1
+    return nproc, affinity, min(blas, affinity)
+
+
+def _oracle_prefill_sample(case, wl, blocks_per_seq):
+    """The oracle on a workload's prefill step: sconv of every token, then
+    attention of whole 256-row blocks of queries (all heads), either every
+    block (``blocks_per_seq`` None) or that many blocks per sequence at
+    stratified positions.  Returns (seconds, attention FLOP computed,
+    estimated seconds of the whole step, rows computed)."""
+    import oracle
     c = case
-    G = c.num_q_heads // c.num_kv_heads
-    T = int(c.q_lens[0])
-    flops = 0
+    T, G = wl.q_len, wl.num_q_heads // wl.num_kv_heads
+    nb = (T + 255) // 256
+    t0 = time.perf_counter()
+    k_new, v_new, _ = oracle.sconv_batch(c.k_pre, c.v_pre, c.conv_w, c.conv_state,
+                                         c.state_slot, c.cu_seqlens)
+    t_sconv = time.perf_counter() - t0
+    done_pairs = 0
     rows_done = 0
-    passes = 0
-    t_start = time.perf_counter()
-    while time.perf_counter() - t_start < budget_s and passes < 8:
-        k_new, v_new, _ = oracle.sconv_batch(c.k_pre, c.v_pre, c.conv_w, c.conv_state,
-                                             c.state_slot, c.cu_seqlens)
-        K = k_new.reshape(T, c.num_kv_heads, HEAD_DIM)
-        V = v_new.reshape(T, c.num_kv_heads, HEAD_DIM)
-        for s in range(0, T, 256):
-            rows = np.arange(s, min(s + 256, T))
-            oracle.relattn_prefill(c.q, K, V, c.bias, c.window, G, rows=rows)
-            n = rows + 1 if c.window == 0 else np.minimum(rows + 1, c.window)
-            flops += int(n.sum()) * 4 * HEAD_DIM * c.num_q_heads
+    t_attn = 0.0
+    for b in range(wl.batch):
+        if blocks_per_seq is None:
+            blocks = range(nb)
+        else:
+            blocks = sorted(set(int(x) for x in
+                                np.linspace(0, nb - 1, blocks_per_seq).round().tolist()))
+        s0 = b * T
+        K = k_new[s0:s0 + T].reshape(T, wl.num_kv_heads, HEAD_DIM)
+        V = v_new[s0:s0 + T].reshape(T, wl.num_kv_heads, HEAD_DIM)
+        for blk in blocks:
+            rows = np.arange(256 * blk, min(256 * blk + 256, T))
+            t1 = time.perf_counter()
+            oracle.relattn_prefill(c.q[s0:s0 + T], K, V, c.bias, wl.window, G, rows=rows)
+            t_attn += time.perf_counter() - t1
+            n = rows + 1 if wl.window == 0 else np.minimum(rows + 1, wl.window)
+            done_pairs += int(n.sum())
             rows_done += len(rows)
-        passes += 1
-    dt = time.perf_counter() - t_start
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{passes} full pass(es) of the workload (sconv of {T} tokens + "
-                      f"attention of all {T} rows x {c.num_q_heads} heads) in {dt:.1f} s, "
-                      f"fp64 numpy"}
+    total_pairs = valid_pairs(wl.q_len, wl.seq_len, wl.window) * wl.batch
+    est = t_sconv + t_attn * total_pairs / done_pairs
+    return (t_sconv + t_attn, 4 * HEAD_DIM * done_pairs * wl.num_q_heads, est, rows_done)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-prefill-32k", action="store_true",
-                    help="skip the 32K full-causal prefill leg")
-    ap.add_argument("--no-mtp", action="store_true",
-                    help="skip the MTP-verification decode leg (it launches the decode kernel "
-                         "with another shape)")
-    ap.add_argument("--no-fp8", action="store_true",
-                    help="skip the decode leg with an FP8 (E4M3) KV cache")
-    ap.add_argument("--no-sconv-out", action="store_true",
-                    help="skip the leg that times the sconv of a plain activation tensor")
-    ap.add_argument("--steady-s", type=float, default=0.3,
-                    help="seconds of untimed back-to-back steps before the warmup steps, "
-                         "so that the timed steps run at the sustained shader clock")
-    ap.add_argument("--copy-bytes", type=int, default=0,
-                    help="after the bench, run one plain device-to-device copy of this "
-                         "many bytes (reference kernel for HBM traffic counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU split is a design note only)", file=sys.stderr)
-        sys.exit(2)
+def _oracle_decode_sample(case, wl, seqs):
+    """The oracle on a decode step for the given sequences: sconv of their new
+    token through the state, then attention of the query over the cached
+    context gathered through the block table (all heads).  Returns
+    (seconds, K+V bytes attended)."""
+    import oracle
+    c = case
+    G = wl.num_q_heads // wl.num_kv_heads
+    H = wl.num_kv_heads
+    t = 0.0
+    nbytes = 0
+    for b in seqs:
+        L = int(c.seq_lens[b])
+        lo = max(0, L - wl.window) if wl.window else 0
+        sl = slice(int(c.cu_seqlens[b]), int(c.cu_seqlens[b + 1]))
+        st = c.conv_state[int(c.state_slot[b])]
+        t0 = time.perf_counter()
+        k_new, _ = oracle.sconv_sequence(c.k_pre[sl], c.conv_w[0], st[0])
+        v_new, _ = oracle.sconv_sequence(c.v_pre[sl], c.conv_w[1], st[1])
+        slots = oracle.slots_for(c.block_table[b], np.arange(lo, L - 1))
+        K = np.zeros((L, H, HEAD_DIM))
+        V = np.zeros((L, H, HEAD_DIM))
+        K[lo:L - 1] = c.past_k[slots]
+        V[lo:L - 1] = c.past_v[slots]
+        K[L - 1] = k_new.reshape(H, HEAD_DIM)
+        V[L - 1] = v_new.reshape(H, HEAD_DIM)
+        oracle.relattn_decode(c.q[b], K, V, c.bias, wl.window, G)
+        t += time.perf_counter() - t0
+        nbytes += (L - lo) * H * HEAD_DIM * 2 * 2
+    return t, nbytes
 
-    import torch
+
+def cpu_baselines(torch, headline_case):
+    """The fp64 oracle timed on the host cores (a reported baseline, not a
+    target): the headline workload on a stratified sample of whole query
+    blocks, extrapolated by pair count; the tiny and 8K prefill workloads in
+    full; the 16K decode on 8 of its 64 sequences and the 1M decode on one of
+    its four, each extrapolated per sequence."""
+    import oracle  # noqa: F401  (the oracle is this leg's whole subject)
     import synth
+    nproc, affinity, cores = _cores()
+    out = {}
+    wl3 = synth.WORKLOADS["full_prefill_32k"]
+    t, fl, est, rows = _oracle_prefill_sample(headline_case, wl3, 3)
+    total = 4 * HEAD_DIM * valid_pairs(wl3.q_len, wl3.seq_len, wl3.window) \
+        * wl3.num_q_heads * wl3.batch
+    out["headline"] = {
+        "value": round(total / est / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+        "nproc": nproc, "affinity": affinity, "kind": "oracle",
+        "sample": f"{wl3.name}: sconv of all {wl3.batch * wl3.q_len} tokens + attention of "
+                  f"{rows} query rows (3 stratified 256-row blocks per sequence, all "
+                  f"{wl3.num_q_heads} heads) in {t:.1f} s; extrapolated by valid pairs to "
+                  f"{est:.0f} s for the whole step; fp64 numpy"}
+    for name in ("tiny_fp32_swa_prefill", "swa_prefill_8k"):
+        wl = synth.WORKLOADS[name]
+        case = synth.workload_case(wl, seed=0)
+        t, fl, est, rows = _oracle_prefill_sample(case, wl, None)
+        out[name] = {"value": round(fl / t / 1e12, 5), "unit": "TFLOP/s", "seconds": round(t, 2),
+                     "cores": cores, "mode": "full", "kind": "oracle",
+                     "sample": f"one whole step: sconv + all {rows} rows x {wl.num_q_heads} heads"}
+        del case
+    for name, nseq in (("swa_decode_16k", 8), ("full_decode_1m", 1)):
+        wl = synth.WORKLOADS[name]
+        case = synth.make_case(wl.dtype, [1] * nseq, [wl.seq_len - 1] * nseq, wl.num_q_heads,
+                               wl.num_kv_heads, wl.window, wl.bias_len, seed=0)
+        t, nbytes = _oracle_decode_sample(case, wl, range(nseq))
+        out[name] = {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "seconds": round(t, 2),
+                     "cores": cores, "mode": "extrapolated", "kind": "oracle",
+                     "est_seconds_full_batch": round(t * wl.batch / nseq, 1),
+                     "sample": f"{nseq} of {wl.batch} sequences: sconv of the new token + "
+                               f"attention over {min(wl.window or wl.seq_len, wl.seq_len)} "
+                               f"keys, all {wl.num_q_heads} heads"}
+        del case
+    head = out.pop("headline")
+    head["other_workloads"] = out
+    return head
 
-    # ---------------- prefill: sconv + prefill on the 8K SWA workload
-    wl = synth.WORKLOADS["swa_prefill_8k"]
+
+# ---------------------------------------------------------------- legs
+def sconv_bytes(c, elem_bytes, cache_elem_bytes=None):
+    """Algorithmic bytes of one K/V sconv call: the pre-conv rows read, the
+    cache rows written, each sequence's 3-row state read and written, and
+    the taps."""
+    cb = elem_bytes if cache_elem_bytes is None else cache_elem_bytes
+    C = c.num_kv_heads * HEAD_DIM
+    n, b = c.num_tokens, len(c.q_lens)
+    return 2 * n * C * elem_bytes + 2 * n * C * cb + 2 * (2 * 3 * C * elem_bytes) * b \
+        + 2 * C * 4 * elem_bytes
+
+
+def time_sconv(torch, dc, steps, warmup):
+    """The K/V sconv + cache write alone (HIP events on its stream)."""
+    def st(ev):
+        if ev is not None:
+            ev[0].record()
+        dc.sconv()
+        if ev is not None:
+            ev[1].record()
+    steady_clocks(torch, st, 0.05)
+    _, ks = time_region(torch, st, None, steps, warmup)
+    ms = float(np.median(ks))
+    nbytes = sconv_bytes(dc.case, 2 if dc.case.dtype == "bf16" else 4, 1 if dc.fp8 else None)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"tokens": dc.case.num_tokens, "sequences": len(dc.case.q_lens),
+            "ms_median": round(ms, 5), "ms_min": round(min(ks), 5), "bytes": nbytes,
+            "achieved": round(gbs, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def prefill_leg(torch, args, name, result_key=None, with_sconv_leg=True):
+    """sconv + prefill steps of a prefill workload.  Returns (summary dict,
+    device case)."""
+    import synth
+    wl = synth.WORKLOADS[name]
     case = synth.workload_case(wl, seed=0)
     dc = DeviceCase(case, torch)
     pairs = valid_pairs(wl.q_len, wl.seq_len, wl.window) * wl.num_q_heads * wl.batch
@@ -373,171 +481,221 @@ def main():
           file=sys.stderr, flush=True)
     n_steady = steady_clocks(torch, step, args.steady_s)
     ms_step, ks = time_region(torch, step, None, args.steps, args.warmup)
-    ms_prefill = sum(ks) / len(ks)
-    value = flop / (ms_step * 1e-3) / 1e12
-    achieved = flop / (ms_prefill * 1e-3) / 1e12
+    ms = sum(ks) / len(ks)
+    tf = flop / (ms * 1e-3) / 1e12
+    prof = f"prefill_bf16_{wl.name}"
+    srcs = ["attention_sconv_amd/csrc/prefill.hip", "attention_sconv_amd/csrc/device_common.h"]
+    summary = {
+        "workload": wl.name + ": " + wl.description + ", paged KV block 128",
+        "ms_per_step": round(ms_step, 4),
+        "step_tflops": round(flop / (ms_step * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(prof + ".traffic.txt", srcs),
+                     "mfma_busy_pct": recorded_field(prof + ".mfma.txt", srcs, "mfma_busy_pct"),
+                     "kernel": "prefill_kernel<bf16>", "ms": round(ms, 4),
+                     "ms_median": round(float(np.median(ks)), 4), "ms_min": round(min(ks), 4),
+                     "algorithmic_flop": flop},
+        "steady_clock_steps": n_steady,
+    }
+    if with_sconv_leg:
+        print(f"[bench] sconv cache write, {wl.name} chunk", file=sys.stderr, flush=True)
+        summary["sconv"] = time_sconv(torch, dc, max(args.steps, 20), args.warmup)
+    return summary, dc, flop
 
+
+def decode_leg(torch, args, name, fp8=False, flush=True):
+    """sconv (one token per sequence) + split-K decode + merge steps of a
+    decode workload, bf16 cache or E4M3 cache (scales 1/64)."""
+    import synth
+    import attention_sconv_amd as ink
+    wl = synth.WORKLOADS[name]
+    case = synth.workload_case(wl, seed=0, past_device="cuda")
+    dd = DeviceCase(case, torch, fp8_scales=(1 / 64, 1 / 64) if fp8 else None)
+    if fp8:
+        dd.setup_decode_mq(torch)
+        fn = dd.decode_fp8
+    else:
+        dd.setup_decode(torch)
+        fn = dd.decode
+    keys = min(wl.window, wl.seq_len) if wl.window else wl.seq_len
+    kv_bytes = wl.batch * wl.num_kv_heads * 2 * keys * HEAD_DIM * (1 if fp8 else 2)
+
+    def dstep(ev):
+        dd.sconv()
+        if ev is not None:
+            ev[0].record()
+        fn()
+        if ev is not None:
+            ev[1].record()
+
+    print(f"[bench] decode {wl.name}{' with an FP8 cache' if fp8 else ''}", file=sys.stderr,
+          flush=True)
+    d_steps = max(args.steps, 20)
+    steady_clocks(torch, dstep, args.steady_s)
+    ms_step, ks = time_region(torch, dstep, None, d_steps, args.warmup)
+    ms = sum(ks) / len(ks)
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    res = {"workload": wl.name + ": " + wl.description
+           + (" with an E4M3 KV cache (scales 1/64)" if fp8 else ""),
+           "ms_per_step": round(ms_step, 4), "ms_decode": round(ms, 4),
+           "ms_decode_median": round(float(np.median(ks)), 4),
+           "ms_decode_min": round(min(ks), 4), "num_splits": dd.num_splits,
+           "kv_bytes": kv_bytes, "achieved": round(gbs, 1), "unit": "GB/s",
+           "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if flush:
+        # the same with a streaming read of 1 GiB before every step, which
+        # evicts the attended K/V from L2 and the 256 MB MALL (clean lines,
+        # so no write-back competes with the decode)
+        fl = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        sink = torch.zeros(ink.PROBE_READ_GROUPS, dtype=torch.float32, device="cuda")
+        _, fks = time_region(torch, dstep, None, d_steps, args.warmup,
+                             between=lambda: ink.inkattn_probe_stream_read(fl, sink))
+        del fl
+        f_ms = float(np.median(fks))
+        f_gbs = kv_bytes / (f_ms * 1e-3) / 1e9
+        res["flushed"] = {"ms_median": round(f_ms, 4), "ms_min": round(min(fks), 4),
+                          "achieved": round(f_gbs, 1), "frac": round(f_gbs / PEAK_HBM_GBS, 4),
+                          "note": "1 GiB streaming read before every step (L2 and MALL "
+                                  "evicted)"}
+    return res, dd, ms
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip every decode leg")
+    ap.add_argument("--no-prefill-8k", action="store_true",
+                    help="skip the 8K sliding-window prefill leg")
+    ap.add_argument("--no-1m", action="store_true", help="skip the 1M-context decode legs")
+    ap.add_argument("--no-mtp", action="store_true",
+                    help="skip the MTP-verification decode leg")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the legs with an FP8 (E4M3) KV cache")
+    ap.add_argument("--no-sconv-out", action="store_true",
+                    help="skip the leg that times the sconv of a plain activation tensor")
+    ap.add_argument("--steady-s", type=float, default=0.3,
+                    help="seconds of untimed back-to-back steps before the warmup steps, "
+                         "so that the timed steps run at the sustained shader clock")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the bench, run one plain device-to-device copy of this "
+                         "many bytes (reference kernel for HBM traffic counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU split is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_sconv_amd as ink
+
+    # ---------------- headline: sconv + prefill on the 32K full-causal workload
+    head, dc, flop = prefill_leg(torch, args, "full_prefill_32k")
+    headline_case = dc.case
+    ms_step = head["ms_per_step"]
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["step_tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name + ": " + wl.description + ", paged KV block 128, "
-                   "step = sconv + prefill", "global_batch": wl.batch,
-                   "seq_len": wl.seq_len, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": recorded_traffic(
-                         "prefill_bf16_swa_prefill_8k.traffic.txt",
-                         ["attention_sconv_amd/csrc/prefill.hip",
-                          "attention_sconv_amd/csrc/device_common.h"]),
-                     "mfma_busy_pct": recorded_field(
-                         "prefill_bf16_swa_prefill_8k.mfma.txt",
-                         ["attention_sconv_amd/csrc/prefill.hip",
-                          "attention_sconv_amd/csrc/device_common.h"], "mfma_busy_pct"),
-                     "kernel": "prefill_kernel<bf16>", "ms": round(ms_prefill, 4),
-                     "ms_median": round(float(np.median(ks)), 4),
-                     "ms_min": round(min(ks), 4),
-                     "algorithmic_flop": flop},
-        "steady_clock_steps": n_steady,
+        "config": {"workload": head["workload"] + ", step = sconv + prefill",
+                   "global_batch": 2, "seq_len": 32768, "parallelism": "none (1 GPU)"},
+        "roofline": head["roofline"],
+        "sconv": head["sconv"],
+        "steady_clock_steps": head["steady_clock_steps"],
     }
+    del dc
+    torch.cuda.empty_cache()
 
-    # ---------------- the 8K SWA prefill step over an E4M3 cache
-    if not args.no_fp8:
-        fcase8 = synth.workload_case(wl, seed=0)
-        fpd = DeviceCase(fcase8, torch, fp8_scales=(1 / 64, 1 / 64))
-        fpd.setup_prefill_fp8(torch)
+    # ---------------- the 8K sliding-window prefill (sconv + prefill)
+    if not args.no_prefill_8k:
+        p8, dc8, flop8 = prefill_leg(torch, args, "swa_prefill_8k")
+        result["config"]["prefill_8k"] = p8["workload"]
+        result["prefill_8k"] = p8
+        del dc8
+        if not args.no_fp8:
+            import synth
+            wl = synth.WORKLOADS["swa_prefill_8k"]
+            fpd = DeviceCase(synth.workload_case(wl, seed=0), torch, fp8_scales=(1 / 64, 1 / 64))
+            fpd.setup_prefill_fp8(torch)
 
-        def fpstep(ev):
-            fpd.sconv()
-            if ev is not None:
-                ev[0].record()
-            fpd.prefill_fp8()
-            if ev is not None:
-                ev[1].record()
+            def fpstep(ev):
+                fpd.sconv()
+                if ev is not None:
+                    ev[0].record()
+                fpd.prefill_fp8()
+                if ev is not None:
+                    ev[1].record()
 
-        print(f"[bench] prefill {wl.name} with an FP8 cache", file=sys.stderr, flush=True)
-        steady_clocks(torch, fpstep, args.steady_s)
-        _, fks = time_region(torch, fpstep, None, args.steps, args.warmup)
-        f_ms = sum(fks) / len(fks)
-        result["prefill_fp8"] = {
-            "workload": wl.name + " with an E4M3 KV cache (scales 1/64)",
-            "ms": round(f_ms, 4), "ms_median": round(float(np.median(fks)), 4),
-            "achieved": round(flop / (f_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-            "frac": round(flop / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "time_vs_bf16_cache": round(f_ms / ms_prefill, 3),
-            "note": "inkattn_relattn_prefill_fp8: page conversion to a bf16 workspace + "
-                    "prefill kernel, both inside the timed call",
-        }
-        del fpd, fcase8
-
-    # ---------------- prefill on the 32K full-causal workload (kernel alone)
-    if not args.no_prefill_32k:
-        del dc
+            print("[bench] prefill swa_prefill_8k with an FP8 cache", file=sys.stderr,
+                  flush=True)
+            steady_clocks(torch, fpstep, args.steady_s)
+            _, fks = time_region(torch, fpstep, None, args.steps, args.warmup)
+            f_ms = sum(fks) / len(fks)
+            p8_ms = p8["roofline"]["ms"]
+            result["prefill_fp8"] = {
+                "workload": wl.name + " with an E4M3 KV cache (scales 1/64)",
+                "ms": round(f_ms, 4), "ms_median": round(float(np.median(fks)), 4),
+                "achieved": round(flop8 / (f_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "frac": round(flop8 / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "time_vs_bf16_cache": round(f_ms / p8_ms, 3),
+                "note": "inkattn_relattn_prefill_fp8: page conversion to a bf16 workspace + "
+                        "prefill kernel, both inside the timed call"}
+            del fpd
         torch.cuda.empty_cache()
-        lwl = synth.WORKLOADS["full_prefill_32k"]
-        print(f"[bench] prefill {lwl.name}", file=sys.stderr, flush=True)
-        lcase = synth.workload_case(lwl, seed=0)
-        dc = DeviceCase(lcase, torch)
-        dc.sconv()
-        l_flop = 4 * HEAD_DIM * valid_pairs(lwl.q_len, lwl.seq_len, lwl.window) \
-            * lwl.num_q_heads * lwl.batch
 
-        def lstep(ev):
-            if ev is not None:
-                ev[0].record()
-            dc.prefill()
-            if ev is not None:
-                ev[1].record()
-
-        steady_clocks(torch, lstep, args.steady_s)
-        _, lks = time_region(torch, lstep, None, 5, 2)
-        l_ms = sum(lks) / len(lks)
-        l_tf = l_flop / (l_ms * 1e-3) / 1e12
-        result["prefill_32k"] = {
-            "workload": lwl.name + ": " + lwl.description + ", paged KV block 128",
-            "kernel": "prefill_kernel<bf16>", "ms": round(l_ms, 3),
-            "ms_median": round(float(np.median(lks)), 3), "algorithmic_flop": l_flop,
-            "achieved": round(l_tf, 1), "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
-            "frac": round(l_tf / PEAK_BF16_TFLOPS, 4),
-            "note": "prefill kernel alone (HIP events), 5 timed launches after 2 warmup",
-        }
-        del lcase
-
-    # ---------------- decode: sconv (1 token/seq) + split-K decode, 16K SWA
+    # ---------------- decode: 16K sliding window (64 sequences)
     if not args.no_decode:
-        del dc
-        torch.cuda.empty_cache()
-        dwl = synth.WORKLOADS["swa_decode_16k"]
-        dcase = synth.workload_case(dwl, seed=0, past_device="cuda")
-        dd = DeviceCase(dcase, torch)
-        dd.setup_decode(torch)
-        kv_bytes = dwl.batch * dwl.num_kv_heads * 2 * min(dwl.window, dwl.seq_len) * HEAD_DIM * 2
-
-        def dstep(ev):
-            dd.sconv()
-            if ev is not None:
-                ev[0].record()
-            dd.decode()
-            if ev is not None:
-                ev[1].record()
-
-        print(f"[bench] decode {dwl.name}", file=sys.stderr, flush=True)
-        d_steps = max(args.steps, 20)
-        steady_clocks(torch, dstep, args.steady_s)
-        d_ms_step, dks = time_region(torch, dstep, None, d_steps, args.warmup)
-        d_ms = sum(dks) / len(dks)
-        gbs = kv_bytes / (d_ms * 1e-3) / 1e9
-        # The same with a streaming read of 1 GiB before every step, which
-        # evicts the attended K/V from L2 and the 256 MB MALL (with clean
-        # lines, so no write-back competes with the decode): decode then
-        # reads HBM.
-        import attention_sconv_amd as ink
-        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        sink = torch.zeros(ink.PROBE_READ_GROUPS, dtype=torch.float32, device="cuda")
-        _, fks = time_region(torch, dstep, None, d_steps, args.warmup,
-                             between=lambda: ink.inkattn_probe_stream_read(flush, sink))
-        del flush
-        f_ms = float(np.median(fks))
-        f_gbs = kv_bytes / (f_ms * 1e-3) / 1e9
-        result["decode"] = {
-            "workload": dwl.name + ": " + dwl.description,
-            "ms_per_step": round(d_ms_step, 4), "ms_decode": round(d_ms, 4),
-            "num_splits": dd.num_splits,
-            "kv_bytes": kv_bytes, "achieved": round(gbs, 1), "unit": "GB/s",
-            "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
-            "ms_decode_median": round(float(np.median(dks)), 4), "ms_decode_min": round(min(dks), 4),
-            "flushed": {"ms_median": round(f_ms, 4), "ms_min": round(min(fks), 4),
-                        "achieved": round(f_gbs, 1), "frac": round(f_gbs / PEAK_HBM_GBS, 4),
-                        "note": "1 GiB streaming read before every step (L2 and MALL evicted)"},
-            "traffic": recorded_traffic(
-                "decode_split_bf16_swa_decode_16k.traffic.txt",
-                ["attention_sconv_amd/csrc/decode.hip",
-                 "attention_sconv_amd/csrc/device_common.h"]),
-            "note": "achieved/frac: back-to-back steps; flushed: L2/MALL evicted before each step",
-        }
+        res, dd, d_ms = decode_leg(torch, args, "swa_decode_16k")
+        res["traffic"] = recorded_traffic("decode_split_bf16_swa_decode_16k.traffic.txt",
+                                          ["attention_sconv_amd/csrc/decode.hip",
+                                           "attention_sconv_amd/csrc/device_common.h"])
+        print("[bench] sconv cache write, one token per sequence", file=sys.stderr, flush=True)
+        res["sconv"] = time_sconv(torch, dd, max(args.steps, 20), args.warmup)
+        result["decode"] = res
         del dd
         torch.cuda.empty_cache()
 
+    # ---------------- decode: 1M full attention (4 sequences, split-K + merge)
+    if not args.no_decode and not args.no_1m:
+        res, dd, m1_ms = decode_leg(torch, args, "full_decode_1m")
+        res["traffic"] = recorded_traffic("decode_split_bf16_full_decode_1m.traffic.txt",
+                                          ["attention_sconv_amd/csrc/decode.hip",
+                                           "attention_sconv_amd/csrc/device_common.h"])
+        res["note"] = "split pass + LSE merge timed together (HIP events around the call)"
+        result["decode_1m"] = res
+        del dd
+        torch.cuda.empty_cache()
+        if not args.no_fp8:
+            res8, dd, m8_ms = decode_leg(torch, args, "full_decode_1m", fp8=True)
+            res8["speedup_vs_bf16_cache"] = round(m1_ms / m8_ms, 3)
+            res8["traffic"] = recorded_traffic("decode_split_fp8_full_decode_1m.traffic.txt",
+                                               ["attention_sconv_amd/csrc/decode.hip",
+                                                "attention_sconv_amd/csrc/device_common.h"])
+            result["decode_1m_fp8"] = res8
+            del dd
+            torch.cuda.empty_cache()
+
     # ---------------- MTP verification: 9 query tokens per sequence
     if not args.no_decode and not args.no_mtp:
+        import synth
         mwl = synth.WORKLOADS["swa_decode_16k_mtp9"]
-        mcase = synth.workload_case(mwl, seed=0, past_device="cuda")
-        md = DeviceCase(mcase, torch)
+        md = DeviceCase(synth.workload_case(mwl, seed=0, past_device="cuda"), torch)
         md.setup_decode_mq(torch)
         m_keys = min(mwl.window + mwl.q_len - 1, mwl.seq_len)
         m_kv_bytes = mwl.batch * mwl.num_kv_heads * 2 * m_keys * HEAD_DIM * 2
-        m_pairs = sum(valid_pairs(mwl.q_len, mwl.seq_len, mwl.window)
-                      for _ in range(mwl.batch)) * mwl.num_q_heads
+        m_pairs = valid_pairs(mwl.q_len, mwl.seq_len, mwl.window) * mwl.batch * mwl.num_q_heads
 
         def mstep(ev):
             md.sconv()
@@ -548,8 +706,9 @@ def main():
                 ev[1].record()
 
         print(f"[bench] decode {mwl.name}", file=sys.stderr, flush=True)
+        d_steps = max(args.steps, 20)
         steady_clocks(torch, mstep, args.steady_s)
-        m_ms_step, mks = time_region(torch, mstep, None, d_steps, args.warmup)
+        _, mks = time_region(torch, mstep, None, d_steps, args.warmup)
         m_ms = sum(mks) / len(mks)
         m_gbs = m_kv_bytes / (m_ms * 1e-3) / 1e9
         result["decode_mtp"] = {
@@ -559,7 +718,6 @@ def main():
             "achieved": round(m_gbs, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
             "frac": round(m_gbs / PEAK_HBM_GBS, 4),
             "tflops": round(4 * HEAD_DIM * m_pairs / (m_ms * 1e-3) / 1e12, 2),
-            "time_vs_one_token_decode": round(m_ms / d_ms, 3),
             "traffic": recorded_traffic(
                 "decode_mq_bf16_swa_decode_16k_mtp9.traffic.txt",
                 ["attention_sconv_amd/csrc/decode_mq.hip",
@@ -567,12 +725,14 @@ def main():
             "note": "inkattn_relattn_decode_mq; the 72 (token, head) columns of a kv-head "
                     "group share one read of its K/V, staged through LDS",
         }
+        if "decode" in result:
+            result["decode_mtp"]["time_vs_one_token_decode"] = round(
+                m_ms / result["decode"]["ms_decode"], 3)
         del md
         torch.cuda.empty_cache()
         if not args.no_fp8:
-            # the same verification step over an E4M3 cache
-            mcase8 = synth.workload_case(mwl, seed=0, past_device="cuda")
-            mf = DeviceCase(mcase8, torch, fp8_scales=(1 / 64, 1 / 64))
+            mf = DeviceCase(synth.workload_case(mwl, seed=0, past_device="cuda"), torch,
+                            fp8_scales=(1 / 64, 1 / 64))
             mf.setup_decode_mq(torch)
 
             def mfstep(ev):
@@ -587,56 +747,35 @@ def main():
             steady_clocks(torch, mfstep, args.steady_s)
             _, mfks = time_region(torch, mfstep, None, d_steps, args.warmup)
             mf_ms = sum(mfks) / len(mfks)
+            mf_gbs = m_kv_bytes / 2 / (mf_ms * 1e-3) / 1e9
             result["decode_mtp"]["fp8_cache"] = {
-                "ms_decode": round(mf_ms, 4), "ms_decode_median": round(float(np.median(mfks)), 4),
-                "kv_bytes": m_kv_bytes // 2,
-                "achieved": round(m_kv_bytes / 2 / (mf_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                "ms_decode": round(mf_ms, 4),
+                "ms_decode_median": round(float(np.median(mfks)), 4),
+                "kv_bytes": m_kv_bytes // 2, "achieved": round(mf_gbs, 1), "unit": "GB/s",
+                "frac": round(mf_gbs / PEAK_HBM_GBS, 4),
                 "speedup_vs_bf16_cache": round(m_ms / mf_ms, 3),
-                "note": "inkattn_relattn_decode_fp8 on the same workload (E4M3 codes, scales 1/64)",
-            }
-            del mf, mcase8
+                "note": "inkattn_relattn_decode_fp8 on the same workload (E4M3 codes, "
+                        "scales 1/64)"}
+            del mf
+            torch.cuda.empty_cache()
 
-    # ---------------- FP8 (E4M3) KV cache: the 16K SWA decode step again
+    # ---------------- E4M3 cache: the 16K sliding-window decode again
     if not args.no_decode and not args.no_fp8:
-        fcase = synth.workload_case(dwl, seed=0, past_device="cuda")
-        fd = DeviceCase(fcase, torch, fp8_scales=(1 / 64, 1 / 64))
-        fd.setup_decode_mq(torch)
-        f_bytes = kv_bytes // 2
-
-        def fstep(ev):
-            fd.sconv()
-            if ev is not None:
-                ev[0].record()
-            fd.decode_fp8()
-            if ev is not None:
-                ev[1].record()
-
-        print(f"[bench] decode {dwl.name} with an FP8 cache", file=sys.stderr, flush=True)
-        steady_clocks(torch, fstep, args.steady_s)
-        f8_ms_step, f8ks = time_region(torch, fstep, None, d_steps, args.warmup)
-        f8_ms = sum(f8ks) / len(f8ks)
-        f8_gbs = f_bytes / (f8_ms * 1e-3) / 1e9
-        result["decode_fp8"] = {
-            "workload": dwl.name + " with an E4M3 KV cache (scales 1/64)",
-            "ms_per_step": round(f8_ms_step, 4), "ms_decode": round(f8_ms, 4),
-            "ms_decode_median": round(float(np.median(f8ks)), 4),
-            "num_splits": fd.num_splits, "kv_bytes": f_bytes,
-            "achieved": round(f8_gbs, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
-            "frac": round(f8_gbs / PEAK_HBM_GBS, 4),
-            "speedup_vs_bf16_cache": round(d_ms / f8_ms, 3),
-            "traffic": recorded_traffic(
-                "decode_split_fp8_swa_decode_16k.traffic.txt",
-                ["attention_sconv_amd/csrc/decode.hip",
-                 "attention_sconv_amd/csrc/device_common.h"]),
-            "note": "inkattn_sconv_fp8 + inkattn_relattn_decode_fp8; bytes = the E4M3 K+V "
-                    "in the attended range",
-        }
-        del fd
+        res, dd, f8_ms = decode_leg(torch, args, "swa_decode_16k", fp8=True, flush=False)
+        if "decode" in result:
+            res["speedup_vs_bf16_cache"] = round(result["decode"]["ms_decode"] / f8_ms, 3)
+        res["traffic"] = recorded_traffic("decode_split_fp8_swa_decode_16k.traffic.txt",
+                                          ["attention_sconv_amd/csrc/decode.hip",
+                                           "attention_sconv_amd/csrc/device_common.h"])
+        res["note"] = ("inkattn_sconv_fp8 + inkattn_relattn_decode_fp8; bytes = the E4M3 K+V "
+                       "in the attended range")
+        result["decode_fp8"] = res
+        del dd
         torch.cuda.empty_cache()
 
-    import attention_sconv_amd as ink
     # ---------------- sconv of a plain activation (attention / MoE output)
     if not args.no_sconv_out:
+        import synth
         sc = synth.make_sconv_out_case("bf16", [8192] * 4, 4096, seed=0, extra_slots=0)
         td = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(
             torch.bfloat16)
@@ -676,13 +815,16 @@ def main():
     print("[bench] measured ceilings", file=sys.stderr, flush=True)
     ceil = ceilings(torch, ink)
     result["ceilings"] = ceil
-    result["roofline"]["frac_of_measured"] = round(achieved / ceil["mfma_bf16_tflops"], 4)
-    if "decode" in result:
-        result["decode"]["frac_of_measured"] = round(gbs / ceil["hbm_read_gbs"], 4)
+    result["roofline"]["frac_of_measured"] = round(
+        result["roofline"]["achieved"] / ceil["mfma_bf16_tflops"], 4)
+    for key in ("decode", "decode_1m"):
+        if key in result:
+            result[key]["frac_of_measured"] = round(result[key]["achieved"]
+                                                    / ceil["hbm_read_gbs"], 4)
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(case)
+        result["cpu_baseline"] = cpu_baselines(torch, headline_case)
 
     if args.copy_bytes > 0:
         n = args.copy_bytes // 4

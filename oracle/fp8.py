@@ -38,6 +38,7 @@ def e4m3_value(code):
 # Non-negative finite magnitudes, ascending: code k (k = 0 .. 126) has value
 # _MAGS[k] (the encoding is monotone in the low 7 bits).
 _MAGS = e4m3_value(np.arange(0x7F))
+_VALUES = e4m3_value(np.arange(256))                   # every code, for dequantize
 
 
 def e4m3_code(x):
@@ -63,5 +64,6 @@ def quantize(x, scale):
 
 
 def dequantize(code, scale):
-    """Values a cache element with these codes reads back as: value * s."""
-    return e4m3_value(code) * float(scale)
+    """Values a cache element with these codes reads back as: value * s
+    (``e4m3_value`` of each code, looked up from the 256 codes' values)."""
+    return _VALUES[np.asarray(code, dtype=np.uint8)] * float(scale)

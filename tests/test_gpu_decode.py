@@ -1,13 +1,16 @@
 """GPU parity of inkattn_relattn_decode (split-K paged decode + LSE merge),
 run after inkattn_sconv has written the new token, against the oracle."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth
-from gpu_util import GpuCase, assert_close, assert_parity, host, oracle_kv, oracle_sconv
+from gpu_util import (GpuCase, assert_attention, assert_close, assert_lse, assert_parity, host,
+                      oracle_kv, oracle_sconv)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,16 +29,16 @@ def _expected(case, seqs=None, lo_window=True):
     return np.stack(outs), np.stack(lses)
 
 
-def _run_and_check(case, num_splits=0, seqs=None):
+def _run_and_check(case, num_splits=0, seqs=None, scale_aware=False):
     gc = GpuCase(case)
     gc.sconv()
     out, lse = gc.decode(num_splits)
     torch.cuda.synchronize()
     want_o, want_l = _expected(case, seqs)
     sel = list(range(len(case.q_lens))) if seqs is None else list(seqs)
-    e1 = assert_parity(host(out)[sel], want_o, case.dtype, "out")
-    e2 = assert_parity(host(lse)[sel], want_l, case.dtype, "lse")
-    return gc, out, lse, (e1, e2)
+    errs = assert_attention(host(out)[sel], want_o, host(lse)[sel], want_l, case.dtype,
+                            "decode", scale_aware)
+    return gc, out, lse, errs
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -88,15 +91,26 @@ def test_decode_swa_16k_full_size():
     # the 16K sliding-window decode workload, every row, auto split count
     wl = synth.WORKLOADS["swa_decode_16k"]
     case = synth.workload_case(wl, seed=0, past_device="cuda")
-    _run_and_check(case)
+    _run_and_check(case, scale_aware=True)
 
 
-def test_decode_full_1m_sampled():
-    # the 1M-key full-attention decode workload; the oracle checks every head
-    # of two sequences (the GPU computes all four)
+def test_decode_full_1m_full_size():
+    # the 1M-key full-attention decode workload, every head of all four
+    # sequences, auto split count (16 splits and the LSE merge).  Outputs are
+    # ~1e-2 and lse ~15 here, so the scale-aware output bound and the
+    # absolute lse bound are what can see a lost or mis-weighted split.
     wl = synth.WORKLOADS["full_decode_1m"]
     case = synth.workload_case(wl, seed=0, past_device="cuda")
-    _run_and_check(case, seqs=[0, 3])
+    _run_and_check(case, scale_aware=True)
+
+
+@pytest.mark.parametrize("name,seqs", [("swa_decode_16k", None), ("full_decode_1m", [0, 3])])
+def test_decode_full_size_shapes_fp32(name, seqs):
+    # the 16K sliding-window and 1M full decode workloads with fp32 storage
+    # (a 16 GiB cache at 1M): the same split counts and merge, held to 1e-5
+    wl = dataclasses.replace(synth.WORKLOADS[name], dtype="fp32")
+    case = synth.workload_case(wl, seed=4, past_device="cuda")
+    _run_and_check(case, seqs=seqs)
 
 
 def test_tiny_fp32_prefill_then_decode_against_oracle():
@@ -143,7 +157,7 @@ def test_tiny_fp32_prefill_then_decode_against_oracle():
         lses.append(lse)
     torch.cuda.synchronize()
     assert_parity(host(torch.cat(outs)), want, "fp32", "prefill + decode outputs")
-    assert_parity(host(torch.cat(lses)), want_lse, "fp32", "prefill + decode lse")
+    assert_lse(host(torch.cat(lses)), want_lse, "fp32", "prefill + decode lse")
 
 
 @pytest.mark.parametrize("W,R", [(1, 1), (1, 300), (129, 1)])

@@ -16,7 +16,7 @@ import torch
 import oracle
 import synth
 from attention_sconv_amd import kvcache
-from gpu_util import (GpuCase, assert_close, assert_parity, fp8_codes, host, oracle_kv,
+from gpu_util import (GpuCase, assert_attention, assert_close, fp8_codes, host, oracle_kv,
                       oracle_sconv)
 
 pytestmark = pytest.mark.gpu
@@ -84,7 +84,7 @@ def _expected(case, gc, seqs=None):
     return np.concatenate(outs), np.concatenate(lses)
 
 
-def _run_and_check(case, scales, num_splits=0, seqs=None):
+def _run_and_check(case, scales, num_splits=0, seqs=None, scale_aware=False):
     gc = GpuCase(case, fp8_scales=scales)
     gc.sconv()
     out, lse = gc.decode_fp8(num_splits)
@@ -95,8 +95,8 @@ def _run_and_check(case, scales, num_splits=0, seqs=None):
     else:
         rows = np.concatenate([np.arange(case.cu_seqlens[b], case.cu_seqlens[b + 1])
                                for b in seqs])
-    assert_parity(host(out)[rows], want_o, "bf16", "out")
-    assert_parity(host(lse)[rows], want_l, "bf16", "lse")
+    assert_attention(host(out)[rows], want_o, host(lse)[rows], want_l, "bf16", "decode_fp8",
+                     scale_aware)
     return gc, out, lse
 
 
@@ -172,7 +172,16 @@ def test_decode_fp8_swa_16k_full_size():
     # the 16K sliding-window decode workload with an FP8 cache, every row
     wl = synth.WORKLOADS["swa_decode_16k"]
     case = synth.workload_case(wl, seed=0, past_device="cuda")
-    _run_and_check(case, (1 / 64, 1 / 64))
+    _run_and_check(case, (1 / 64, 1 / 64), scale_aware=True)
+
+
+def test_decode_fp8_full_1m_full_size():
+    # the 1M-key full-attention decode workload over an E4M3 cache (half the
+    # 8 GiB of the bf16 cache), every head of all four sequences, auto split
+    # count and the LSE merge
+    wl = synth.WORKLOADS["full_decode_1m"]
+    case = synth.workload_case(wl, seed=0, past_device="cuda")
+    _run_and_check(case, (1 / 64, 1 / 64), scale_aware=True)
 
 
 def _run_prefill_and_check(case, scales):
@@ -181,8 +190,7 @@ def _run_prefill_and_check(case, scales):
     out, lse = gc.prefill_fp8()
     torch.cuda.synchronize()
     want_o, want_l = _expected(case, gc)
-    assert_parity(host(out), want_o, "bf16", "out")
-    assert_parity(host(lse), want_l, "bf16", "lse")
+    assert_attention(host(out), want_o, host(lse), want_l, "bf16", "prefill_fp8")
     return gc, out, lse
 
 

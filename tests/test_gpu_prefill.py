@@ -1,13 +1,15 @@
 """GPU parity of inkattn_relattn_prefill (run after inkattn_sconv has written
 the new tokens' keys and values) against the oracle."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth
-from gpu_util import GpuCase, assert_close, assert_parity, host, oracle_kv, oracle_sconv
+from gpu_util import GpuCase, assert_attention, assert_close, host, oracle_kv, oracle_sconv
 
 pytestmark = pytest.mark.gpu
 
@@ -36,14 +38,14 @@ def _expected(case, rows_per_seq=None, stored_kv=False):
     return np.concatenate(toks), np.concatenate(outs), np.concatenate(lses)
 
 
-def _run_and_check(case, rows_per_seq=None, stored_kv=False):
+def _run_and_check(case, rows_per_seq=None, stored_kv=False, scale_aware=False):
     gc = GpuCase(case)
     gc.sconv()
     out, lse = gc.prefill()
     torch.cuda.synchronize()
     toks, want_o, want_l = _expected(case, rows_per_seq, stored_kv)
-    assert_parity(host(out)[toks], want_o, case.dtype, "out")
-    assert_parity(host(lse)[toks], want_l, case.dtype, "lse")
+    assert_attention(host(out)[toks], want_o, host(lse)[toks], want_l, case.dtype, "prefill",
+                     scale_aware)
     return gc, out, lse
 
 
@@ -136,28 +138,44 @@ def test_prefill_deterministic_and_block_placement_invariant():
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
-def _sample_rows(q_len, seed):
+def _late_rows(q_len, n, seed):
+    """About n distinct rows of a chunk: tile and window edges, the last 64
+    rows, and random rows whose density grows toward the end of the chunk
+    (late rows attend the most keys, so their outputs are the smallest)."""
     rng = np.random.default_rng(seed)
-    fixed = [0, 1, 2, 3, 63, 64, 127, 128, 129, 2047, 2048, 2049, 4095, 4096,
-             q_len - 129, q_len - 128, q_len - 2, q_len - 1]
+    fixed = [0, 1, 2, 3, 63, 64, 127, 128, 129, 255, 256, 257, 2047, 2048, 2049, 4095, 4096,
+             q_len // 2, q_len - 257, q_len - 256, q_len - 129, q_len - 128]
     rows = set(r for r in fixed if 0 <= r < q_len)
-    rows.update(rng.integers(0, q_len, 24).tolist())
-    return sorted(rows)
+    rows.update(range(max(0, q_len - 64), q_len))
+    while len(rows) < min(n, q_len):
+        u = rng.random(n)
+        rows.update((q_len - 1 - np.floor(q_len * u * u)).astype(np.int64).tolist())
+    return np.array(sorted(rows))
 
 
-def test_prefill_swa_8k_full_size_sampled():
-    # batch 1, T=8192, Hq=32, Hkv=4, window 2048, R=2048, bf16; the GPU computes
-    # every row, the oracle checks ~40 rows (all heads) across tile edges.
+def test_prefill_swa_8k_full_size():
+    # batch 1, T=8192, Hq=32, Hkv=4, window 2048, R=2048, bf16: every row of
+    # every head against the oracle, with the scale-aware bound as well
     wl = synth.WORKLOADS["swa_prefill_8k"]
     case = synth.workload_case(wl, seed=0)
-    _run_and_check(case, rows_per_seq=lambda b, n: _sample_rows(n, 1 + b))
+    _run_and_check(case, scale_aware=True)
 
 
 def test_prefill_full_32k_full_size_sampled():
-    # batch 2, T=32768, full causal, R=32768, bf16
+    # batch 2, T=32768, full causal, R=32768, bf16: 512 rows per sequence,
+    # weighted toward the late rows (up to 32K keys, outputs ~0.04), all heads
     wl = synth.WORKLOADS["full_prefill_32k"]
     case = synth.workload_case(wl, seed=0)
-    _run_and_check(case, rows_per_seq=lambda b, n: _sample_rows(n, 7 + b))
+    _run_and_check(case, rows_per_seq=lambda b, n: _late_rows(n, 512, 7 + b), scale_aware=True)
+
+
+@pytest.mark.parametrize("name,rows", [("swa_prefill_8k", 256), ("full_prefill_32k", 128)])
+def test_prefill_full_size_shapes_fp32(name, rows):
+    # the 8K sliding-window and 32K full-causal workloads with fp32 storage:
+    # the same tiling, splits of work and merges as bf16, held to 1e-5
+    wl = dataclasses.replace(synth.WORKLOADS[name], dtype="fp32")
+    case = synth.workload_case(wl, seed=3)
+    _run_and_check(case, rows_per_seq=lambda b, n: _late_rows(n, rows, 11 + b))
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
