@@ -14,6 +14,9 @@
 * ``inkattn_relattn_prefill``  -- relative-position GQA attention over new
                                  tokens (bf16/fp32 MFMA, sheared bias band);
 * ``inkattn_relattn_decode``   -- split-K paged decode plus log-sum-exp merge;
+* ``inkattn_relattn_decode_noalloc`` -- the same with its split partials in a
+                                 static device array (for callers that cannot
+                                 allocate);
 * ``inkattn_relattn_decode_mq`` -- the same for a few query tokens per sequence
                                  (verification of multi-token-prediction drafts).
 
@@ -26,9 +29,10 @@ torch device tensors (torch supplies memory and streams only).  The helpers in
 """
 
 from ._lib import (  # noqa: F401
-    BF16, FP32, OK, EINVAL, ENOTSUP, EHIP, EXPORTED, LIB_PATH,
+    BF16, FP32, OK, EINVAL, ENOTSUP, EHIP, ESCRATCH, EXPORTED, LIB_PATH, NOALLOC_SCRATCH_BYTES,
     AttnDesc, InkattnError, make_desc, status_string,
     inkattn_sconv, inkattn_relattn_prefill, inkattn_relattn_decode,
+    inkattn_relattn_decode_noalloc,
     inkattn_relattn_decode_num_splits, inkattn_relattn_decode_workspace_size,
     inkattn_sconv_paged, inkattn_sconv_out, inkattn_sconv_fp8, inkattn_relattn_decode_fp8,
     inkattn_relattn_decode_mq, inkattn_relattn_decode_mq_num_splits,

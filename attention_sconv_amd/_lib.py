@@ -14,7 +14,8 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libinkattn.so")
 
-OK, EINVAL, ENOTSUP, EHIP = 0, 1, 2, 3
+OK, EINVAL, ENOTSUP, EHIP, ESCRATCH = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 8 << 20       # INKATTN_NOALLOC_SCRATCH_BYTES
 FP32, BF16 = 0, 1
 
 EXPORTED = (
@@ -29,6 +30,7 @@ EXPORTED = (
     "inkattn_relattn_decode_num_splits",
     "inkattn_relattn_decode_workspace_size",
     "inkattn_relattn_decode",
+    "inkattn_relattn_decode_noalloc",
     "inkattn_relattn_decode_mq_num_splits",
     "inkattn_relattn_decode_mq_workspace_size",
     "inkattn_relattn_decode_mq",
@@ -95,6 +97,9 @@ def _load():
     lib.inkattn_relattn_decode.argtypes = [dp, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                            i32, vp, sz, vp]
     lib.inkattn_relattn_decode.restype = i32
+    lib.inkattn_relattn_decode_noalloc.argtypes = [dp, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp,
+                                                   vp, i32, vp]
+    lib.inkattn_relattn_decode_noalloc.restype = i32
     lib.inkattn_relattn_decode_mq_num_splits.argtypes = [dp, i32, i32, i32]
     lib.inkattn_relattn_decode_mq_num_splits.restype = i32
     lib.inkattn_relattn_decode_mq_workspace_size.argtypes = [dp, i32, i32, i32, i32, i32]
@@ -202,6 +207,16 @@ def inkattn_relattn_decode(desc, num_seqs, max_seq_len, q, k_cache, v_cache, blo
                                      _ptr(lse), num_splits, _ptr(workspace), workspace_bytes,
                                      _stream(stream))
     _check(st, "inkattn_relattn_decode")
+
+
+def inkattn_relattn_decode_noalloc(desc, num_seqs, max_seq_len, q, k_cache, v_cache,
+                                   block_table, max_blocks_per_seq, seq_lens, bias, out, lse,
+                                   num_splits, stream=None):
+    st = _lib.inkattn_relattn_decode_noalloc(ctypes.byref(desc), num_seqs, max_seq_len, _ptr(q),
+                                             _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                             max_blocks_per_seq, _ptr(seq_lens), _ptr(bias),
+                                             _ptr(out), _ptr(lse), num_splits, _stream(stream))
+    _check(st, "inkattn_relattn_decode_noalloc")
 
 
 def inkattn_probe_mfma_bf16(num_groups, iters, out, stream=None):

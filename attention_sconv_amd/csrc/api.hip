@@ -102,6 +102,26 @@ bool decode_grid_too_large(const inkattn_attn_desc_t* d, int64_t num_seqs, int64
 
 inkattn_status_t from_hip(hipError_t e) { return e == hipSuccess ? INKATTN_OK : INKATTN_EHIP; }
 
+// Scratch of inkattn_relattn_decode_noalloc: each GPU the library runs on
+// holds its own copy of this array until the process ends.
+__device__ __align__(256) unsigned char scratch[INKATTN_NOALLOC_SCRATCH_BYTES];
+
+// The device address of `scratch` on the current device, taken once per
+// device with that device current (nullptr if the runtime cannot say).
+void* scratch_on_current_device() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+    return nullptr;
+  addr[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -112,6 +132,7 @@ const char* inkattn_status_string(int32_t status) {
     case INKATTN_EINVAL: return "invalid argument";
     case INKATTN_ENOTSUP: return "unsupported configuration";
     case INKATTN_EHIP: return "HIP runtime error";
+    case INKATTN_ESCRATCH: return "request exceeds the library's static scratch buffer";
     default: return "unknown status";
   }
 }
@@ -316,6 +337,47 @@ size_t inkattn_relattn_decode_workspace_size(const inkattn_attn_desc_t* desc,
   return rows * 128 * sizeof(float) + ((rows * sizeof(float) + 15) & ~(size_t)15);
 }
 
+// Host checks of a one-token decode (every argument but the workspace);
+// *splits receives the split count the call runs with.
+static inkattn_status_t decode_check(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                     int32_t max_seq_len, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_table,
+                                     int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                     const void* bias, const void* out, int32_t num_splits,
+                                     int32_t* splits) {
+  inkattn_status_t st = check_desc(desc);
+  if (st != INKATTN_OK) return st;
+  if (num_seqs < 0 || max_seq_len < 0 || num_splits < 0) return INKATTN_EINVAL;
+  *splits = 0;
+  if (num_seqs == 0) return INKATTN_OK;
+  if (max_seq_len < 1 || max_blocks_per_seq < 1) return INKATTN_EINVAL;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !bias || !out)
+    return INKATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return INKATTN_EINVAL;
+  if (bias_table_too_large(desc)) return INKATTN_ENOTSUP;
+  const int32_t s = num_splits == 0 ? auto_splits(desc, num_seqs, max_seq_len) : num_splits;
+  if (decode_grid_too_large(desc, num_seqs, num_seqs, s, 1)) return INKATTN_ENOTSUP;
+  *splits = s;
+  return INKATTN_OK;
+}
+
+// Launch of a checked one-token decode; the partial results of its splits
+// (when there are several) go to `workspace`.
+static inkattn_status_t decode_launch(const inkattn_attn_desc_t* desc, int32_t num_seqs,
+                                      const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, const void* bias, void* out,
+                                      float* lse, int32_t s, void* workspace, void* stream) {
+  const size_t rows = (size_t)num_seqs * desc->num_q_heads * (size_t)s;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = part_o + rows * 128;
+  return from_hip(inkattn::launch_decode(shape_of(desc), num_seqs, num_seqs, 1, s, q, k_cache,
+                                         v_cache, block_table, max_blocks_per_seq, nullptr,
+                                         seq_lens, bias, out, lse, part_o, part_lse, nullptr,
+                                         (hipStream_t)stream));
+}
+
 inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t num_seqs,
                                         int32_t max_seq_len, const void* q,
                                         const void* k_cache, const void* v_cache,
@@ -324,28 +386,16 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
                                         const void* bias, void* out, float* lse,
                                         int32_t num_splits, void* workspace,
                                         size_t workspace_bytes, void* stream) {
-  inkattn_status_t st = check_desc(desc);
-  if (st != INKATTN_OK) return st;
-  if (num_seqs < 0 || max_seq_len < 0 || num_splits < 0) return INKATTN_EINVAL;
-  if (num_seqs == 0) return INKATTN_OK;
-  if (max_seq_len < 1 || max_blocks_per_seq < 1) return INKATTN_EINVAL;
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !bias || !out || !workspace)
-    return INKATTN_EINVAL;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-      !aligned16(workspace))
-    return INKATTN_EINVAL;
-  if (bias_table_too_large(desc)) return INKATTN_ENOTSUP;
-  const int32_t s = num_splits == 0 ? auto_splits(desc, num_seqs, max_seq_len) : num_splits;
-  if (decode_grid_too_large(desc, num_seqs, num_seqs, s, 1)) return INKATTN_ENOTSUP;
+  int32_t s = 0;
+  inkattn_status_t st = decode_check(desc, num_seqs, max_seq_len, q, k_cache, v_cache,
+                                     block_table, max_blocks_per_seq, seq_lens, bias, out,
+                                     num_splits, &s);
+  if (st != INKATTN_OK || num_seqs == 0) return st;
+  if (!workspace || !aligned16(workspace)) return INKATTN_EINVAL;
   const size_t need = inkattn_relattn_decode_workspace_size(desc, num_seqs, max_seq_len, s);
   if (workspace_bytes < need) return INKATTN_EINVAL;
-  const size_t rows = (size_t)num_seqs * desc->num_q_heads * (size_t)s;
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = part_o + rows * 128;
-  return from_hip(inkattn::launch_decode(shape_of(desc), num_seqs, num_seqs, 1, s, q, k_cache,
-                                         v_cache, block_table, max_blocks_per_seq, nullptr,
-                                         seq_lens, bias, out, lse, part_o, part_lse, nullptr,
-                                         (hipStream_t)stream));
+  return decode_launch(desc, num_seqs, q, k_cache, v_cache, block_table, max_blocks_per_seq,
+                       seq_lens, bias, out, lse, s, workspace, stream);
 }
 
 int32_t inkattn_relattn_decode_mq_num_splits(const inkattn_attn_desc_t* desc, int32_t num_seqs,
@@ -444,6 +494,38 @@ inkattn_status_t inkattn_relattn_decode_fp8(const inkattn_attn_desc_t* desc, int
   return decode_mq_common(desc, num_seqs, num_tokens, max_q_len, max_seq_len, q, k_cache,
                           v_cache, block_table, max_blocks_per_seq, cu_seqlens_q, seq_lens, bias,
                           out, lse, num_splits, workspace, workspace_bytes, scales, stream);
+}
+
+// The decode that allocates nothing: its split partials live in `scratch`,
+// a static device array of INKATTN_NOALLOC_SCRATCH_BYTES.  Host code never
+// passes the array's name to a kernel (on the host it is a stand-in, not a
+// device address); it takes the array's address on the current device once
+// through hipGetSymbolAddress and uses that.  Every call on one device
+// shares that device's array.
+inkattn_status_t inkattn_relattn_decode_noalloc(const inkattn_attn_desc_t* desc,
+                                                int32_t num_seqs, int32_t max_seq_len,
+                                                const void* q, const void* k_cache,
+                                                const void* v_cache, const int32_t* block_table,
+                                                int32_t max_blocks_per_seq,
+                                                const int32_t* seq_lens, const void* bias,
+                                                void* out, float* lse, int32_t num_splits,
+                                                void* stream) {
+  int32_t s = 0;
+  inkattn_status_t st = decode_check(desc, num_seqs, max_seq_len, q, k_cache, v_cache,
+                                     block_table, max_blocks_per_seq, seq_lens, bias, out,
+                                     num_splits, &s);
+  if (st != INKATTN_OK || num_seqs == 0) return st;
+  // One split writes the output directly and uses no partials.
+  const size_t need =
+      s > 1 ? inkattn_relattn_decode_workspace_size(desc, num_seqs, max_seq_len, s) : 0;
+  if (need > (size_t)INKATTN_NOALLOC_SCRATCH_BYTES) return INKATTN_ESCRATCH;
+  void* ws = nullptr;
+  if (s > 1) {
+    ws = scratch_on_current_device();
+    if (ws == nullptr) return INKATTN_EHIP;
+  }
+  return decode_launch(desc, num_seqs, q, k_cache, v_cache, block_table, max_blocks_per_seq,
+                       seq_lens, bias, out, lse, s, ws, stream);
 }
 
 }  // extern "C"

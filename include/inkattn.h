@@ -18,7 +18,8 @@
  * - All array arguments are DEVICE pointers into memory the caller owns.
  *   The library never allocates, frees or synchronises; every launch is
  *   asynchronous on `stream` (a hipStream_t passed as void*, NULL = the null
- *   stream).  The library keeps no global state and is thread-safe.
+ *   stream).  The library keeps no global state and is thread-safe, except
+ *   the static scratch array of inkattn_relattn_decode_noalloc (see there).
  * - Scalar arguments (counts, maxima) are host values.
  * - Storage dtype INKATTN_FP32 (float) or INKATTN_BF16 (bfloat16 bits);
  *   all arithmetic is fp32.  q, K/V, conv weights/state, bias and out share
@@ -53,8 +54,13 @@ typedef enum {
   INKATTN_OK = 0,
   INKATTN_EINVAL = 1,
   INKATTN_ENOTSUP = 2,
-  INKATTN_EHIP = 3
+  INKATTN_EHIP = 3,
+  INKATTN_ESCRATCH = 4    /* inkattn_relattn_decode_noalloc: the request's split
+                             partials exceed INKATTN_NOALLOC_SCRATCH_BYTES */
 } inkattn_status_t;
+
+/* Size of the static device scratch of inkattn_relattn_decode_noalloc. */
+#define INKATTN_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 typedef enum { INKATTN_FP32 = 0, INKATTN_BF16 = 1 } inkattn_dtype_t;
 
@@ -247,6 +253,34 @@ inkattn_status_t inkattn_relattn_decode(const inkattn_attn_desc_t* desc, int32_t
                                         const void* bias, void* out, float* lse,
                                         int32_t num_splits, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/* inkattn_relattn_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments (minus workspace
+ * and workspace_bytes), same computation and kernels, same result.
+ *   The split partials live in a static device array of
+ *   INKATTN_NOALLOC_SCRATCH_BYTES (8 MiB) inside the library, which every GPU
+ *   the library runs on holds until the process ends; the call itself
+ *   allocates nothing.  They take inkattn_relattn_decode_workspace_size(...)
+ *   bytes for the split count used (none with one split): at 8 MiB about
+ *   16,000 (sequence, q-head, split) rows, e.g. 4 x 1M-key sequences with
+ *   Hq = 32 at the automatic 16 splits use 1 MiB.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in
+ *   time on one GPU (other streams, other host threads) race and may return
+ *   wrong results.  Calls ordered on one stream are safe; nothing in the
+ *   array needs clearing between calls (each call writes every partial it
+ *   reads).
+ * Errors as inkattn_relattn_decode; INKATTN_ESCRATCH when the partials of
+ * the split count used exceed the array (pass fewer splits); INKATTN_EHIP
+ * when the runtime cannot give the array's device address. */
+inkattn_status_t inkattn_relattn_decode_noalloc(const inkattn_attn_desc_t* desc,
+                                                int32_t num_seqs, int32_t max_seq_len,
+                                                const void* q, const void* k_cache,
+                                                const void* v_cache, const int32_t* block_table,
+                                                int32_t max_blocks_per_seq,
+                                                const int32_t* seq_lens, const void* bias,
+                                                void* out, float* lse, int32_t num_splits,
+                                                void* stream);
 
 /* Decode of several query tokens per sequence at once: the verification
  * step of multi-token prediction, where a sequence's last accepted token and

@@ -37,6 +37,7 @@ def test_status_strings():
     assert "invalid" in ink.status_string(1)
     assert "unsupported" in ink.status_string(2)
     assert "HIP" in ink.status_string(3)
+    assert "scratch" in ink.status_string(4)
     assert ink.status_string(99) == "unknown status"
 
 
@@ -127,6 +128,43 @@ def test_decode_workspace_rules():
     st = lib.inkattn_relattn_decode(ctypes.byref(d), B, L, FAKE, FAKE, FAKE, FAKE, 128, FAKE,
                                     FAKE, FAKE, None, 0, FAKE + 4, need, None)
     assert st == ink.EINVAL
+
+
+@pytest.mark.parametrize("kw,status", BAD_DESCS)
+def test_decode_noalloc_rejects_bad_desc(kw, status):
+    lib = ink._lib._lib
+    d = _desc(**kw)
+    st = lib.inkattn_relattn_decode_noalloc(ctypes.byref(d), 1, 100, FAKE, FAKE, FAKE, FAKE, 1,
+                                            FAKE, FAKE, FAKE, None, 0, None)
+    assert st == status
+
+
+def test_decode_noalloc_rejects_partials_beyond_its_scratch():
+    # 64 sequences x 32 heads x 16 splits of partials (16.9 MB) exceed the
+    # 8 MiB static scratch: rejected before anything runs; the same call with
+    # a workspace of its own is accepted by the host checks of the plain decode
+    lib = ink._lib._lib
+    d = _desc(W=0, R=1 << 20)
+    B, L, S = 64, 1 << 20, 16
+    need = ink.inkattn_relattn_decode_workspace_size(d, B, L, S)
+    assert need > ink.NOALLOC_SCRATCH_BYTES
+    st = lib.inkattn_relattn_decode_noalloc(ctypes.byref(d), B, L, FAKE, FAKE, FAKE, FAKE, 8192,
+                                            FAKE, FAKE, FAKE, None, S, None)
+    assert st == ink.ESCRATCH
+    for bad in (dict(num_splits=-1), dict(num_seqs=-1)):
+        args = dict(num_seqs=B, num_splits=S)
+        args.update(bad)
+        st = lib.inkattn_relattn_decode_noalloc(ctypes.byref(d), args["num_seqs"], L, FAKE, FAKE,
+                                                FAKE, FAKE, 8192, FAKE, FAKE, FAKE, None,
+                                                args["num_splits"], None)
+        assert st == ink.EINVAL
+    # misaligned output
+    st = lib.inkattn_relattn_decode_noalloc(ctypes.byref(d), 1, L, FAKE, FAKE, FAKE, FAKE, 8192,
+                                            FAKE, FAKE, FAKE + 4, None, 4, None)
+    assert st == ink.EINVAL
+    # nothing to do is a no-op
+    assert lib.inkattn_relattn_decode_noalloc(ctypes.byref(d), 0, L, None, None, None, None, 1,
+                                              None, None, None, None, 0, None) == ink.OK
 
 
 def test_num_splits_heuristic():
