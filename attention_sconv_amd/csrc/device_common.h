@@ -117,21 +117,6 @@ template <> struct Frag8<bf16> {
     }
     return f;
   }
-  // acc + sum of the 8 (rounded) elements, two per v_dot2_f32_bf16 against
-  // (1.0, 1.0).  Written as inline VOP3P: with the builtin, the compiler in
-  // ROCm 7.2 emits the VOP2 form v_dot2c_f32_bf16 and, when the source is a
-  // word of a 128-bit register tuple, reads the tuple's first register for
-  // every word.
-  __device__ __forceinline__ float sum_into(float acc) const {
-    const uint32_t ones = 0x3f803f80u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float r;
-      asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(r) : "v"(v[i]), "v"(ones), "v"(acc));
-      acc = r;
-    }
-    return acc;
-  }
   __device__ __forceinline__ bf16x8_t as_mfma() const {
     return __builtin_bit_cast(bf16x8_t, v);
   }
@@ -164,9 +149,6 @@ template <> struct Frag8<float> {
     f.lo = f32x4{x[0], x[1], x[2], x[3]};
     f.hi = f32x4{x[4], x[5], x[6], x[7]};
     return f;
-  }
-  __device__ __forceinline__ float sum_into(float acc) const {
-    return acc + ((lo[0] + lo[1]) + (lo[2] + lo[3])) + ((hi[0] + hi[1]) + (hi[2] + hi[3]));
   }
   __device__ __forceinline__ Frag8 keep_first(int n) const {
     Frag8 f;

@@ -131,6 +131,22 @@ __device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds, uint32_t vof
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
+// Four 16-byte buffer loads into LDS under one M0 value: load j writes lane
+// l's bytes at LDS lds + 1024 j + 16 l.  The instruction offset 1024 j is
+// added to the memory address too, so the caller passes voff_j less 1024 j
+// (on a descriptor that starts 4 KiB early, so the difference stays
+// positive).  Rewriting M0 before every load costs the issuing wave about
+// 110 cycles per load (it waits for the previous load's use of M0); one M0
+// per four loads issues them at the memory pipeline's rate.
+__device__ __forceinline__ void lds_dma16x4(u32x4 rsrc, uint32_t lds, uint32_t v0, uint32_t v1,
+                                            uint32_t v2, uint32_t v3, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\t"
+               "buffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
+               "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
+               "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
+               "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
+               :: "s"(lds), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(rsrc), "s"(soff) : "memory");
+}
 // An empty asm that reads a fragment: forces its load to have completed here.
 __device__ __forceinline__ void keep_live(const Frag8<bf16>& f) { asm volatile("" :: "v"(f.v)); }
 __device__ __forceinline__ void keep_live(const Frag8<float>& f) {
@@ -294,10 +310,54 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
       lds_dma4(btab_rsrc, lds_addr(&sm.pages[x & 1][0]), (uint32_t)(jt * kBK / kPage) * 4u, 0u);
     }
   };
+  // Which 1 KiB blocks of a tile loader lw fetches.  bf16: a run of four
+  // consecutive blocks 4 lw .. 4 lw + 3 under one M0 value, and block
+  // 16 + lw when the tile has it (K 17 blocks, V^T 18); fp32: blocks
+  // lw, lw + 4, lw + 8, ...
+  constexpr bool kRuns = sizeof(T) == 2;
+  static_assert(!kRuns || (kKLoads >= 16 && kKLoads <= 20 && kVLoads >= 16 && kVLoads <= 20 &&
+                           kKPer == 5 && kVPer == 5),
+                "run layout of the bf16 tiles");
+  auto my_block = [&](int j) { return kRuns ? (j < 4 ? 4 * lw + j : 16 + lw) : lw + kLoaders * j; };
+  auto page_rsrc_early = [&](const T* cache, int phys) {          // starts 4 KiB before the page
+    return make_buf_rsrc(reinterpret_cast<const char*>(
+                             cache + ((size_t)phys * A.Hkv + kvg) * (size_t)(kPage * kHeadDim)) - 4096,
+                         kPageBytes + 4096u);
+  };
   // Tile loads of stage x, on page numbers published earlier.
   auto dma_tiles = [&](int x, int k_phys, int v_phys) {
     if (lw < 0) return;                           // only waves 4-7 load
     const int ln = lane;                          // (per-lane offsets are loop-invariant)
+    if constexpr (kRuns) {
+      auto koff = [&](int n) {
+        const int slot = 64 * n + ln;
+        const int row = slot / kKRowSlots, ch = min(slot % kKRowSlots, kKDataSlots - 1);
+        return (uint32_t)(row * kHeadDim * (int)sizeof(T) + ch * kSlotBytes);
+      };
+      auto voff = [&](int n) {
+        const int slot = 64 * n + ln;
+        const int row = slot / kVRowSlots, ch = min(slot % kVRowSlots, kVDataSlots - 1);
+        return (uint32_t)(row * kPage * (int)sizeof(T) + ch * kSlotBytes);
+      };
+      const int n0 = 4 * lw;
+      if (x < n_t) {                                 // K of tile x: one run + block 16 + lw
+        const int jt = jt_lo + x;
+        const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(jt * kBK % kPage) * kHeadDim * sizeof(T));
+        const uint32_t lds = lds_addr(&sm.k[x & 1][0]);
+        lds_dma16x4(page_rsrc_early(kc, k_phys), lds + 1024u * n0, koff(n0) + 4096u,
+                    koff(n0 + 1) + 3072u, koff(n0 + 2) + 2048u, koff(n0 + 3) + 1024u, soff);
+        if (16 + lw < kKLoads) lds_dma16(page_rsrc(kc, k_phys), lds + 1024u * (16 + lw), koff(16 + lw), soff);
+      }
+      if (x >= 1) {                                  // V of tile x-1: the same
+        const int jt = jt_lo + x - 1;
+        const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(jt * kBK % kPage) * sizeof(T));
+        const uint32_t lds = lds_addr(&sm.vt[(x - 1) & 1][0]);
+        lds_dma16x4(page_rsrc_early(vc, v_phys), lds + 1024u * n0, voff(n0) + 4096u,
+                    voff(n0 + 1) + 3072u, voff(n0 + 2) + 2048u, voff(n0 + 3) + 1024u, soff);
+        if (16 + lw < kVLoads) lds_dma16(page_rsrc(vc, v_phys), lds + 1024u * (16 + lw), voff(16 + lw), soff);
+      }
+      return;
+    }
     if (x < n_t) {                                   // K of tile x
       const int jt = jt_lo + x;
       const u32x4 r = page_rsrc(kc, k_phys);
@@ -344,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
       char* buf = reinterpret_cast<char*>(&sm.k[x & 1][0]);
 #pragma unroll
       for (int j = 0; j < kKPer; ++j) {
-        const int n = lw + kLoaders * j;
+        const int n = my_block(j);
         const int slot = 64 * n + ln;
         if (n < kKLoads && slot / kKRowSlots >= n_tail)
           *reinterpret_cast<u32x4*>(buf + kSlotBytes * slot) = u32x4{0, 0, 0, 0};
@@ -355,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
       constexpr int kPer = kSlotBytes / (int)sizeof(T);          // keys per 16-byte slot
 #pragma unroll
       for (int j = 0; j < kVPer; ++j) {
-        const int n = lw + kLoaders * j;
+        const int n = my_block(j);
         const int slot = 64 * n + ln;
         const int ch = slot % kVRowSlots;
         if (n < kVLoads && ch < kVDataSlots && kPer * (ch + 1) > n_tail) {
@@ -507,6 +567,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
       m_used = need ? m_tile : m_used;
     }
     const float msub = m_used == -INFINITY ? 0.0f : m_used;
+    // The row sum adds the fp32 probabilities on the vector ALU, in four
+    // independent chains.  (v_dot2_f32_bf16 over the packed values would
+    // take one instruction per pair, but it does not co-issue with the
+    // other wave's MFMAs: each one waits for the matrix core, which
+    // doubled this phase when it ran beside a matrix phase.)
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -515,8 +581,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = fast_exp2(acc[t][8 * hh + e] * c - msub);
         pf[2 * t + hh] = Frag8<T>::pack(p);
-        l_sum = pf[2 * t + hh].sum_into(l_sum);     // sums the values fed to P V
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ls[e & 3] += p[e];
       }
+    l_sum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
   // V buffer 1 is read (times P^T = 0) by the first matrix phase before any
