@@ -32,7 +32,7 @@ level.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--steady-s S]
                        [--no-cpu-baseline] [--no-prefill-8k] [--no-decode]
-                       [--no-1m] [--no-mtp] [--no-fp8] [--no-sconv-out]
+                       [--no-1m] [--no-16k] [--no-mtp] [--no-fp8] [--no-sconv-out]
 """
 
 import argparse
@@ -501,6 +501,9 @@ def prefill_leg(torch, args, name, result_key=None, with_sconv_leg=True):
     if with_sconv_leg:
         print(f"[bench] sconv cache write, {wl.name} chunk", file=sys.stderr, flush=True)
         summary["sconv"] = time_sconv(torch, dc, max(args.steps, 20), args.warmup)
+        summary["sconv"]["traffic"] = recorded_traffic(
+            f"sconv_write_bf16_{wl.name}.traffic.txt",
+            ["attention_sconv_amd/csrc/sconv.hip", "attention_sconv_amd/csrc/device_common.h"])
     return summary, dc, flop
 
 
@@ -571,6 +574,8 @@ def main():
     ap.add_argument("--no-prefill-8k", action="store_true",
                     help="skip the 8K sliding-window prefill leg")
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-context decode legs")
+    ap.add_argument("--no-16k", action="store_true",
+                    help="skip the 16K sliding-window decode legs (bf16 and E4M3 cache)")
     ap.add_argument("--no-mtp", action="store_true",
                     help="skip the MTP-verification decode leg")
     ap.add_argument("--no-fp8", action="store_true",
@@ -656,7 +661,7 @@ def main():
         torch.cuda.empty_cache()
 
     # ---------------- decode: 16K sliding window (64 sequences)
-    if not args.no_decode:
+    if not args.no_decode and not args.no_16k:
         res, dd, d_ms = decode_leg(torch, args, "swa_decode_16k")
         res["traffic"] = recorded_traffic("decode_split_bf16_swa_decode_16k.traffic.txt",
                                           ["attention_sconv_amd/csrc/decode.hip",
@@ -673,7 +678,11 @@ def main():
         res["traffic"] = recorded_traffic("decode_split_bf16_full_decode_1m.traffic.txt",
                                           ["attention_sconv_amd/csrc/decode.hip",
                                            "attention_sconv_amd/csrc/device_common.h"])
-        res["note"] = "split pass + LSE merge timed together (HIP events around the call)"
+        res["merge_traffic"] = recorded_traffic("decode_merge_bf16_full_decode_1m.traffic.txt",
+                                                ["attention_sconv_amd/csrc/decode.hip",
+                                                 "attention_sconv_amd/csrc/device_common.h"])
+        res["note"] = ("split pass + LSE merge timed together (HIP events around the call); "
+                       "traffic: the split kernel, merge_traffic: the merge kernel")
         result["decode_1m"] = res
         del dd
         torch.cuda.empty_cache()
@@ -760,7 +769,7 @@ def main():
             torch.cuda.empty_cache()
 
     # ---------------- E4M3 cache: the 16K sliding-window decode again
-    if not args.no_decode and not args.no_fp8:
+    if not args.no_decode and not args.no_fp8 and not args.no_16k:
         res, dd, f8_ms = decode_leg(torch, args, "swa_decode_16k", fp8=True, flush=False)
         if "decode" in result:
             res["speedup_vs_bf16_cache"] = round(result["decode"]["ms_decode"] / f8_ms, 3)
