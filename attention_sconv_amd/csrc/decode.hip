@@ -68,9 +68,18 @@ template <> struct ItemRegs<bf16, fp8e4, false> {
   u32x4 k[4];
   u32x2 v[8];
 };
+// The 64-key E4M3 item also carries this lane's 16 bias entries, packed two
+// to a dword.  Its keys j0 .. j0+15 are distances pos-j0 .. pos-j0-15, 16
+// consecutive entries of one bias row: fetched as 18 entries (9 dwords) from
+// the even entry at or below the smallest, and aligned by `par` when used.
+// Entries past R-1 are replaced by bias[R-1] where they are used; the one
+// item per sequence whose distances reach below 15 while still visible (it
+// holds the query position) has its entries fetched again one by one there.
 template <> struct ItemRegs<bf16, fp8e4, true> {
   u32x4 k[8];
   u32x4 v[8];
+  uint32_t bw[9];
+  uint32_t par;
 };
 
 // TKV: the cache element type, T or fp8e4 (bf16 queries only).  An E4M3 cache
@@ -173,6 +182,10 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
     for (int dt = 0; dt < 8; ++dt) o[u][dt] = f32x4{0, 0, 0, 0};
   }
   const float c = 0.08838834764831845f * kLog2e * k_scale;   // log2(e) / sqrt(128)
+  // bias[h][R-1] of this lane's head (the entry every distance past the
+  // table takes), for the E4M3 items' bias runs
+  const float bias_last = kWide ? to_f32(buf_load_elem<T>(bias_r, (bias_row[0] + R - 1) * sizeof(T)))
+                                : 0.0f;
 
   auto page_base = [&](int blk) -> size_t {
     const int phys = block_table[(size_t)b * max_blocks + blk];
@@ -199,12 +212,28 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
     const int blk = my_hi - 1 - (item >> kIL);
     const int qu = item & ((1 << kIL) - 1);
     const int j0 = blk * kPage + kIK * qu + kKL * grp;
+    if constexpr (kWide) {
+      // (a run that starts before the table, in the newest item of head 0,
+      // reads as zeros: such items are fetched again where they are used)
+      const int first = (int)bias_row[0] + pos[0] - j0 - (kKL - 1);
+      ir.par = (uint32_t)first & 1u;
+      const uint32_t off = ((uint32_t)first & ~1u) * (uint32_t)sizeof(T);
+      const u32x4 w0 = buf_load16(bias_r, off, 0);
+      const u32x4 w1 = buf_load16(bias_r, off + 16, 0);
 #pragma unroll
-    for (int u = 0; u < kCT; ++u)
+      for (int i = 0; i < 4; ++i) {
+        ir.bw[i] = w0[i];
+        ir.bw[4 + i] = w1[i];
+      }
+      ir.bw[8] = __builtin_amdgcn_raw_buffer_load_b32(bias_r, off + 32, 0, 0);
+    } else {
 #pragma unroll
-      for (int e = 0; e < kKL; ++e)
-        bb[u][e] = buf_load_elem<T>(
-            bias_r, (bias_row[u] + min(max(pos[u] - (j0 + e), 0), R - 1)) * sizeof(T));
+      for (int u = 0; u < kCT; ++u)
+#pragma unroll
+        for (int e = 0; e < kKL; ++e)
+          bb[u][e] = buf_load_elem<T>(
+              bias_r, (bias_row[u] + min(max(pos[u] - (j0 + e), 0), R - 1)) * sizeof(T));
+    }
     const size_t base = page_base(blk);
     const rsrc_t kr = make_rsrc(k_cache + base, kPageBytes);
     const rsrc_t vr = make_rsrc(v_cache + base, kPageBytes);
@@ -273,13 +302,41 @@ __global__ __launch_bounds__(64 * kW, 1) void decode_split_kernel(
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) sacc[t] = mfma16(k_frag(ir, t, ds), qf[0][ds], sacc[t]);
     }
+    // Bias of key j0 + e: entry t = 15 - e of the aligned run, the low half
+    // of dword t/2 for even t, the high half for odd t.  The shift goes
+    // through an empty asm so that the alignment stays here, after the
+    // item's loads have been waited for, and is not moved up to them.
+    float bf[kKL];
+    if constexpr (kWide) {
+      uint32_t sh = 16u * ir.par;
+      asm volatile("" : "+v"(sh));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t a = __builtin_amdgcn_alignbit(ir.bw[i + 1], ir.bw[i], sh);
+        bf[15 - 2 * i] = __uint_as_float(a << 16);
+        bf[14 - 2 * i] = __uint_as_float(a & 0xffff0000u);
+      }
+      const int top = pos[0] - j0;                 // distance of key j0
+      if (__any(top > R - 1)) {                    // distances past the table: bias[R-1]
+#pragma unroll
+        for (int e = 0; e < kKL; ++e) bf[e] = top - e > R - 1 ? bias_last : bf[e];
+      }
+      if (__any(top < kKL - 1 && top >= 0)) {      // the item that holds the query position
+#pragma unroll
+        for (int e = 0; e < kKL; ++e) {
+          const float v = to_f32(buf_load_elem<T>(
+              bias_r, (bias_row[0] + min(max(top - e, 0), R - 1)) * sizeof(T)));
+          bf[e] = top < kKL - 1 ? v : bf[e];
+        }
+      }
+    }
     float x[kKL];
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < kKL; ++e) {
       const int j = j0 + e;
       const bool ok = head_ok[0] && j >= k_lo[0] && j <= pos[0];
-      x[e] = ok ? sacc[e >> 2][e & 3] * c + to_f32(bb[0][e]) * kLog2e : -INFINITY;
+      x[e] = ok ? sacc[e >> 2][e & 3] * c + bf[e] * kLog2e : -INFINITY;
       mx = fmaxf(mx, x[e]);
     }
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
