@@ -8,15 +8,20 @@
 // (the last W-1 tokens are kept).  The cached rows are the pre-convolution
 // inputs; tap 3 weights the current token.
 //
-// Work split: grid (token chunk, sequence, K|V); each thread owns 8
-// consecutive channels (one 16-byte bf16 vector, two for fp32), so a wave
-// reads a 1 KiB channel-contiguous row per token (Hkv = 4), and 8 tokens of
-// one sequence, loading them and the 3-token halo up front so the loads are
-// in flight together; the 4-tap window then runs in registers.  Only the
-// thread that handles a sequence's first chunk touches that sequence's
-// state, so the in-place state update is race-free.
-// Memory-bound: every input byte is read once (plus a 3-row halo per chunk)
-// and every output byte written once.
+// Work split: a wave covers 64 tokens x 64 channels of one sequence, lane l
+// the tokens 8*(l%8) .. +7 and the channels 8*(l/8) .. +7 of that block
+// (one 16-byte bf16 vector of each token, two for fp32).  It loads the 8
+// tokens and the 3-token halo before them up front, so all loads are in
+// flight together and the halo rows are ones its neighbouring lanes read
+// too; the 4-tap window then runs in registers.  With this lane order one
+// store instruction of the transposed V cache writes 8 rows x 64 tokens,
+// whole 128-byte lines, and a K-cache store 8 tokens x 64 channels.  Work-
+// groups are dealt so that those one XCD runs together are neighbours in the
+// token order (their halos come from that XCD's L2).  Only the lane that
+// handles a sequence's first chunk touches that sequence's state, so the
+// in-place state update is race-free.
+// Memory-bound: every input byte is read once (plus a 3-row halo per 8
+// tokens, mostly from the caches) and every output byte written once.
 //
 // Paged state (kPaged): the pre-convolution rows of every token are kept in a
 // paged cache of their own, [block][128 tokens][Hkv*128 channels], addressed
@@ -34,12 +39,20 @@
 namespace inkattn {
 
 constexpr int kSconvTok = 8;          // tokens per thread
-constexpr int kSconvRows = 4;         // token chunks per work-group (blockDim.y)
-// At most 256 threads per work-group: a thread holds 11 rows of 8 channels
-// and 64 fp32 outputs, which needs more than the 128 VGPRs a 1024-thread
-// bound leaves (that bound made the kernels spill).  Channels beyond 256
-// threads' worth go to further work-groups along grid z.
+// 256 threads per work-group: a thread holds 11 rows of 8 channels and 64
+// fp32 outputs, more than the 128 VGPRs a 1024-thread bound leaves.
 constexpr int kSconvThreads = 256;
+// K/V cache write: a work-group covers 128 tokens x one head (128 channels)
+// of K or V, waves (token half, channel half).  Output sconv: 64 tokens x 256
+// channels, waves side by side in channels.
+constexpr int kWriteTok = 128;
+constexpr int kOutTok = 64;
+constexpr int kOutCh = 256;
+
+// Work-group id -> linear work index.  The dispatcher deals ids round-robin
+// over the 8 XCDs; index (id % 8) * per + id / 8 gives each XCD a contiguous
+// range of the work, token blocks fastest.
+__device__ __forceinline__ int xcd_work_index(int id, int per) { return (id & 7) * per + (id >> 3); }
 
 // Paged-state arguments (unused by the dense-state kernel).
 struct SconvPaged {
@@ -58,13 +71,20 @@ __global__ __launch_bounds__(kSconvThreads) void sconv_cache_write_kernel(
     const T* __restrict__ conv_w, T* __restrict__ conv_state,
     const int32_t* __restrict__ state_slot, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ slot_mapping, TC* __restrict__ k_cache,
-    TC* __restrict__ v_cache, SconvPaged pg, float inv_scale_k, float inv_scale_v) {
+    TC* __restrict__ v_cache, SconvPaged pg, float inv_scale_k, float inv_scale_v, int ntb,
+    int num_seqs, int per) {
   constexpr bool kFp8 = std::is_same<TC, fp8e4>::value;
-  const int ncg = gridDim.z >> 1;            // channel groups
-  const int which = blockIdx.z / ncg;        // 0 = keys, 1 = values
-  const int b = blockIdx.y;
-  const int r0 = (blockIdx.x * blockDim.y + threadIdx.y) * kSconvTok;   // first token (relative)
-  const int c0 = ((blockIdx.z % ncg) * blockDim.x + threadIdx.x) * 8;
+  // work index -> (token block, sequence, K|V and head)
+  const int wi = xcd_work_index(blockIdx.x, per);
+  if (wi >= ntb * num_seqs * 2 * Hkv) return;
+  const int tb = wi % ntb;
+  const int b = (wi / ntb) % num_seqs;
+  const int z = wi / (ntb * num_seqs);
+  const int which = z / Hkv;                 // 0 = keys, 1 = values
+  const int head = z % Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = kWriteTok * tb + 64 * (wave >> 1) + kSconvTok * (lane & 7);   // first token (relative)
+  const int c0 = kHeadDim * head + 64 * (wave & 1) + 8 * (lane >> 3);
   const int t_begin = cu_seqlens[b];
   const int n = cu_seqlens[b + 1] - t_begin;
   if (r0 >= n || c0 >= C) return;
@@ -216,10 +236,17 @@ template <typename T>
 __global__ __launch_bounds__(kSconvThreads) void sconv_out_kernel(
     int C, const T* __restrict__ x_in, const T* __restrict__ conv_w, T* __restrict__ conv_state,
     const int32_t* __restrict__ state_slot, const int32_t* __restrict__ cu_seqlens,
-    T* __restrict__ y_out) {
-  const int b = blockIdx.y;
-  const int r0 = (blockIdx.x * blockDim.y + threadIdx.y) * kSconvTok;   // first token (relative)
-  const int c0 = (blockIdx.z * blockDim.x + threadIdx.x) * 8;
+    T* __restrict__ y_out, int ntb, int num_seqs, int per) {
+  // work index -> (token block, sequence, channel block)
+  const int wi = xcd_work_index(blockIdx.x, per);
+  const int ncb = (C + kOutCh - 1) / kOutCh;
+  if (wi >= ntb * num_seqs * ncb) return;
+  const int tb = wi % ntb;
+  const int b = (wi / ntb) % num_seqs;
+  const int cb = wi / (ntb * num_seqs);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = kOutTok * tb + kSconvTok * (lane & 7);                 // first token (relative)
+  const int c0 = kOutCh * cb + 64 * wave + 8 * (lane >> 3);
   const int t_begin = cu_seqlens[b];
   const int n = cu_seqlens[b + 1] - t_begin;
   if (r0 >= n || c0 >= C) return;
@@ -274,17 +301,19 @@ __global__ __launch_bounds__(kSconvThreads) void sconv_out_kernel(
 hipError_t launch_sconv_out(int dtype, int C, int num_seqs, int max_chunk_len, const void* x,
                             const void* conv_w, void* conv_state, const int32_t* state_slot,
                             const int32_t* cu_seqlens, void* y, hipStream_t stream) {
-  dim3 block(min(C / 8, kSconvThreads), 1);
-  block.y = (unsigned)max(1, min(kSconvRows, kSconvThreads / (int)block.x));
-  dim3 grid((max_chunk_len + kSconvTok * block.y - 1) / (kSconvTok * block.y), num_seqs,
-            (C / 8 + block.x - 1) / block.x);
+  const int ntb = (max_chunk_len + kOutTok - 1) / kOutTok;
+  const long work = (long)ntb * num_seqs * ((C + kOutCh - 1) / kOutCh);
+  if (work > 0x7ffffff0L) return hipErrorInvalidConfiguration;
+  const int per = (int)((work + 7) / 8);
+  const dim3 grid((unsigned)(8L * per)), block(kSconvThreads);
   if (dtype == kDtypeBf16)
     hipLaunchKernelGGL(sconv_out_kernel<bf16>, grid, block, 0, stream, C, (const bf16*)x,
-                       (const bf16*)conv_w, (bf16*)conv_state, state_slot, cu_seqlens, (bf16*)y);
+                       (const bf16*)conv_w, (bf16*)conv_state, state_slot, cu_seqlens, (bf16*)y,
+                       ntb, num_seqs, per);
   else
     hipLaunchKernelGGL(sconv_out_kernel<float>, grid, block, 0, stream, C, (const float*)x,
                        (const float*)conv_w, (float*)conv_state, state_slot, cu_seqlens,
-                       (float*)y);
+                       (float*)y, ntb, num_seqs, per);
   return hipGetLastError();
 }
 
@@ -296,11 +325,11 @@ hipError_t launch_sconv_any(int dtype, int Hkv, int num_seqs, int max_chunk_len,
                             void* k_cache, void* v_cache, const SconvPaged& pg,
                             const float* fp8_scales, hipStream_t stream) {
   const int C = Hkv * kHeadDim;
-  dim3 block(min(C / 8, kSconvThreads), 1);
-  block.y = (unsigned)max(1, min(kSconvRows, kSconvThreads / (int)block.x));
-  const int ncg = (C / 8 + block.x - 1) / block.x;           // channel groups (Hkv > 16)
-  dim3 grid((max_chunk_len + kSconvTok * block.y - 1) / (kSconvTok * block.y), num_seqs,
-            2 * ncg);
+  const int ntb = (max_chunk_len + kWriteTok - 1) / kWriteTok;
+  const long work = (long)ntb * num_seqs * 2 * Hkv;
+  if (work > 0x7ffffff0L) return hipErrorInvalidConfiguration;
+  const int per = (int)((work + 7) / 8);
+  const dim3 grid((unsigned)(8L * per)), block(kSconvThreads);
   auto go = [&](auto t_tag, auto c_tag) {
     using T = decltype(t_tag);
     using TC = decltype(c_tag);
@@ -309,7 +338,7 @@ hipError_t launch_sconv_any(int dtype, int Hkv, int num_seqs, int max_chunk_len,
     hipLaunchKernelGGL((sconv_cache_write_kernel<T, TC, kPaged>), grid, block, 0, stream, C,
                        Hkv, (const T*)k_in, (const T*)v_in, (const T*)conv_w, (T*)conv_state,
                        state_slot, cu_seqlens, slot_mapping, (TC*)k_cache, (TC*)v_cache, pg,
-                       ik, iv);
+                       ik, iv, ntb, num_seqs, per);
   };
   if constexpr (!kPaged) {
     if (fp8_scales != nullptr) {
