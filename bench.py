@@ -19,8 +19,9 @@ Further legs in the same JSON line:
   decode_mtp     MTP verification: 9 query tokens per sequence, 16K window
   decode_fp8     the 16K decode over an E4M3 cache
   sconv_out      the sconv of a plain [tokens][channels] activation
-  ceilings       a dense bf16 MFMA loop (with its shader clock) and a 4 GiB
-                 streaming read, measured in the same job
+  ceilings       a dense bf16 MFMA loop (with its shader clock), a 4 GiB
+                 streaming read and a 1 GiB device copy, measured in the
+                 same job
   cpu_baseline   the fp64 oracle on the host cores: the headline workload on
                  a stratified sample (extrapolated by pair count), the tiny
                  and 8K prefill in full, the 16K and 1M decode on some of
@@ -284,13 +285,25 @@ def ceilings(torch, ink):
     e[1].record()
     torch.cuda.synchronize()
     gbs = nbytes * reps / (e[0].elapsed_time(e[1]) * 1e-3) / 1e9
-    del buf
+    # read + write: a device-to-device copy of 1 GiB (the runtime's copy
+    # kernel), bytes read plus bytes written per second
+    half = buf[: (1 << 30) // 4]
+    dst = torch.empty_like(half)
+    dst.copy_(half)
+    e[0].record()
+    for _ in range(reps):
+        dst.copy_(half)
+    e[1].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * reps / (e[0].elapsed_time(e[1]) * 1e-3) / 1e9
+    del buf, half, dst
     torch.cuda.empty_cache()
     return {"mfma_bf16_tflops": round(mfma, 1), "sclk_mhz_under_mfma": round(sclk),
-            "hbm_read_gbs": round(gbs, 1),
+            "hbm_read_gbs": round(gbs, 1), "hbm_copy_gbs": round(copy_gbs, 1),
             "note": "inkattn_probe_mfma_bf16 (1024 groups x 8 waves x 8 chains of "
-                    "32x32x16 bf16) and inkattn_probe_stream_read (4 GiB, 256 groups x "
-                    "256 threads x 8 loads of 16 B in flight), same job"}
+                    "32x32x16 bf16), inkattn_probe_stream_read (4 GiB, 256 groups x "
+                    "256 threads x 8 loads of 16 B in flight) and a 1 GiB device copy "
+                    "(read + write bytes), same job"}
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -826,10 +839,16 @@ def main():
     result["ceilings"] = ceil
     result["roofline"]["frac_of_measured"] = round(
         result["roofline"]["achieved"] / ceil["mfma_bf16_tflops"], 4)
-    for key in ("decode", "decode_1m"):
+    # read-only legs against the streaming-read ceiling, the sconv legs (as
+    # many bytes written as read) against the copy ceiling
+    for key in ("decode", "decode_1m", "decode_1m_fp8", "decode_fp8", "decode_mtp"):
         if key in result:
             result[key]["frac_of_measured"] = round(result[key]["achieved"]
                                                     / ceil["hbm_read_gbs"], 4)
+    for leg in (result.get("sconv"), result.get("prefill_8k", {}).get("sconv"),
+                result.get("decode", {}).get("sconv"), result.get("sconv_out")):
+        if leg:
+            leg["frac_of_copy"] = round(leg["achieved"] / ceil["hbm_copy_gbs"], 4)
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
