@@ -32,7 +32,10 @@ pages this library is built from):
 * ``fp8``        -- the OCP E4M3 code of a scaled key or value and what a
   cached code reads back as, for an FP8 KV cache (news article, *Roadmap*:
   FP8 for the global-attention layers).  Attention over such a cache is the
-  attention above on the read-back keys and values.
+  attention above on the read-back keys and values.  For FP8 matrix
+  products: the per-tile query quantizer and, in ``attention``, the bound
+  on what rounding the probabilities to E4M3 can move
+  (``relattn_prefill_p8_bounds``).
 
 Everything is evaluated in float64 straight from the definitions: no tiling,
 no online softmax, no splits.  Inputs may be float32 or bfloat16-representable
@@ -50,6 +53,7 @@ from .attention import (  # noqa: F401
     visible_key_range,
     relattn_rows,
     relattn_prefill,
+    relattn_prefill_p8_bounds,
     relattn_decode,
     lse_merge,
 )

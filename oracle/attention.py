@@ -89,9 +89,9 @@ def relattn_rows(q_rows, positions, K, V, bias, window, num_q_heads_per_kv,
     return out, lse
 
 
-def _relattn_block(Q, K, V, bias_h, positions, window, key_lo, key_hi):
-    """Same definition as :func:`relattn_rows` for one query head and a block
-    of rows, written as matrix products (rows are still independent)."""
+def _block_logits(Q, K, bias_h, positions, window, key_lo, key_hi):
+    """Logits [rows, keys] of one query head for keys key_lo .. key_hi-1, -inf
+    where a key is not visible (the definition of :func:`relattn_rows`)."""
     i = positions[:, None]
     j = np.arange(key_lo, key_hi)[None, :]
     R = bias_h.shape[0]
@@ -102,7 +102,13 @@ def _relattn_block(Q, K, V, bias_h, positions, window, key_lo, key_hi):
         visible &= dist <= window - 1
     logits = (Q @ K[key_lo:key_hi].T) / math.sqrt(d)
     logits = logits + bias_h[np.clip(dist, 0, R - 1)]
-    logits = np.where(visible, logits, -np.inf)
+    return np.where(visible, logits, -np.inf)
+
+
+def _relattn_block(Q, K, V, bias_h, positions, window, key_lo, key_hi):
+    """Same definition as :func:`relattn_rows` for one query head and a block
+    of rows, written as matrix products (rows are still independent)."""
+    logits = _block_logits(Q, K, bias_h, positions, window, key_lo, key_hi)
     m = logits.max(axis=1, keepdims=True)
     e = np.exp(logits - m)
     den = e.sum(axis=1, keepdims=True)
@@ -144,6 +150,75 @@ def relattn_prefill(q, K, V, bias, window, num_q_heads_per_kv, q_start=None,
             out[c0:c0 + len(sel), h] = o
             lse[c0:c0 + len(sel), h] = l
     return out, lse
+
+
+def relattn_prefill_p8_bounds(q, K, V, bias, window, num_q_heads_per_kv, q_start=None,
+                              rows=None, row_block=256):
+    """:func:`relattn_prefill` plus the error that rounding the softmax
+    probabilities to E4M3 (ties to even, row sums over the rounded values)
+    can cause, for FP8 matrix products.
+
+    With p_j = exp(logit_j - max) and a kernel running maximum anywhere in
+    [max - 8 ln 2, max] (so its probabilities are lambda * p_j, 1 <= lambda
+    <= 256), the rounding moves lambda * p_j by at most half an E4M3 step,
+    which relative to the row sum lambda * sum p is at most
+    h_j = max(p_j / 8, 2^-9) / 2 / sum p (the step is at most a value's 1/8
+    among normals, and 2^-9 among subnormals).  The output O = sum w_j v_j
+    then moves by sum_j e_j (v_j - O) / sum p^ with |e_j| <= h_j sum p, so
+
+      bound_o = sum_j h_j |v_j - O| / (1 - sum_j h_j)        (per dimension)
+      sigma_o = sqrt(sum_j h_j^2 / 3 (v_j - O)^2)            (errors uniform
+                                                              in +-h_j)
+      bound_l = -log(1 - sum_j h_j),  sigma_l = sqrt(sum_j h_j^2 / 3)
+
+    for the log-sum-exp.  Returns (out, lse, bound_o, sigma_o, bound_l,
+    sigma_l), shapes as :func:`relattn_prefill` ([rows, Hq, d] and [rows, Hq]).
+    """
+    q = np.asarray(q)
+    T, Hq, d = q.shape
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    bias = np.asarray(bias, dtype=np.float64)
+    L = K.shape[0]
+    if q_start is None:
+        q_start = L - T
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    n = len(rows)
+    out, bo, so = (np.zeros((n, Hq, d)) for _ in range(3))
+    lse, bl, sl = (np.zeros((n, Hq)) for _ in range(3))
+    for c0 in range(0, n, row_block):
+        sel = rows[c0:c0 + row_block]
+        pos = q_start + sel
+        lo = 0 if window == 0 else max(0, int(pos.min()) - window + 1)
+        hi = int(pos.max()) + 1
+        for h in range(Hq):
+            g = h // num_q_heads_per_kv
+            logits = _block_logits(q[sel, h, :].astype(np.float64), K[:, g, :], bias[h], pos,
+                                   window, lo, hi)
+            m = logits.max(axis=1, keepdims=True)
+            p = np.exp(logits - m)
+            den = p.sum(axis=1, keepdims=True)
+            Vb = V[lo:hi, g, :]
+            o = (p @ Vb) / den
+            hrel = np.where(p > 0, np.maximum(p / 8.0, 2.0 ** -9) / 2.0, 0.0) / den
+            hsum = hrel.sum(axis=1)
+            # sum_j h_j |v_j - O|, over blocks of rows and keys (memory)
+            babs = np.zeros_like(o)
+            for r0 in range(0, len(sel), 32):
+                for k0 in range(0, Vb.shape[0], 512):
+                    dev = np.abs(Vb[None, k0:k0 + 512, :] - o[r0:r0 + 32, None, :])
+                    babs[r0:r0 + 32] += np.einsum("rk,rkd->rd", hrel[r0:r0 + 32, k0:k0 + 512], dev)
+            # sum_j a_j (v_j - O)^2 = sum a v^2 - 2 O sum a v + O^2 sum a
+            a = hrel ** 2 / 3.0
+            var = a @ (Vb * Vb) - 2.0 * o * (a @ Vb) + o * o * a.sum(axis=1, keepdims=True)
+            sl_ = slice(c0, c0 + len(sel))
+            out[sl_, h] = o
+            lse[sl_, h] = (m + np.log(den))[:, 0]
+            bo[sl_, h] = babs / (1.0 - hsum)[:, None]
+            so[sl_, h] = np.sqrt(np.maximum(var, 0.0))
+            bl[sl_, h] = -np.log1p(-hsum)
+            sl[sl_, h] = np.sqrt((hrel ** 2 / 3.0).sum(axis=1))
+    return out, lse, bo, so, bl, sl
 
 
 def relattn_decode(q, K, V, bias, window, num_q_heads_per_kv):

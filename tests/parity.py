@@ -23,6 +23,12 @@ unit scale) and how each is applied:
 * lse: absolute, ``1e-5`` (fp32) or ``2e-2`` (bf16).  lse is computed in
   fp32 either way; in bf16 it moves only through the rounding of the stored
   keys (about 1e-3 in the logits).
+* FP8 matrix products (``check_p8``): the oracle computes the attention on
+  the same quantised queries, keys and values, and bounds what rounding the
+  softmax probabilities to E4M3 can move (``relattn_prefill_p8_bounds``):
+  every output within that bound plus bf16 output rounding
+  (``2^-8 |want| + 1e-4``), every lse within its bound plus 1e-4, and the
+  root mean square of the errors, in units of the predicted spread, below 2.
 """
 
 import numpy as np
@@ -98,3 +104,23 @@ def check_attention(got_o, want_o, got_l, want_l, dtype, what="", scale_aware=Fa
         print(f"[parity] {what}: max |out err| {e_o:.3e}, max |lse err| {e_l:.3e}"
               + (f", max row relative L2 {rel:.3e}" if rel is not None else ""), flush=True)
     return (e_o, e_l) if rel is None else (e_o, e_l, rel)
+
+
+def check_p8(got_o, got_l, exp, what="fp8 products"):
+    """Bounds for FP8 matrix products; ``exp`` = the six arrays of
+    ``oracle.relattn_prefill_p8_bounds`` (out, lse, bound_o, sigma_o,
+    bound_l, sigma_l)."""
+    o, l, bo, so, bl, sl = (np.asarray(x, dtype=np.float64) for x in exp)
+    got_o, o = _arrays(got_o, o)
+    got_l, l = _arrays(got_l, l)
+    assert np.isfinite(got_o).all() and np.isfinite(got_l).all(), f"{what}: non-finite values"
+    err = got_o - o
+    _verdict(np.abs(err), bo + 2.0 ** -8 * np.abs(o) + 1e-4, got_o, o, f"{what} out")
+    z = err / (so + 2.0 ** -9 * np.abs(o) / np.sqrt(3.0) + 1e-6)
+    rms = float(np.sqrt(np.mean(z ** 2)))
+    assert rms < 2.0, f"{what}: output errors are {rms:.2f} predicted spreads (rms)"
+    el = got_l - l
+    _verdict(np.abs(el), bl + 1e-4, got_l, l, f"{what} lse")
+    rmsl = float(np.sqrt(np.mean((el / (sl + 2e-5)) ** 2)))
+    assert rmsl < 2.0, f"{what}: lse errors are {rmsl:.2f} predicted spreads (rms)"
+    return rms, rmsl

@@ -10,10 +10,11 @@ from the oracle only by the roundings a bf16 cache and bf16 output make."""
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import synth
-from parity import check_attention, check_lse, check_out, check_out_scaled
+from parity import check_attention, check_lse, check_out, check_out_scaled, check_p8
 
 L = 1 << 20          # keys: the 1M-context full-attention decode
 G = 8                # q-heads of one kv-head group
@@ -106,3 +107,49 @@ def test_checker_accepts_stored_kv_roundings_on_prefill_rows():
     with pytest.raises(AssertionError):
         check_attention(bad_o, o, bad_l, l, "bf16", "dropped keys", scale_aware=True)
     assert np.isfinite(bad_l[-1]).all()
+
+
+def _p8_case():
+    rng = np.random.default_rng(11)
+    L, T = 900, 48
+    q = rng.standard_normal((T, 4, 128))
+    K = rng.standard_normal((L, 1, 128))
+    V = rng.standard_normal((L, 1, 128))
+    bias = rng.standard_normal((4, 400)) * 0.5
+    exp = oracle.relattn_prefill_p8_bounds(q, K, V, bias, 0, 4)
+    return q, K, V, bias, exp
+
+
+def _bf16(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+def test_p8_checker_accepts_rounded_probabilities():
+    # the exact result with the probabilities rounded to E4M3 at a random
+    # running-maximum scale (oracle encoder) and the output rounded to bf16
+    q, K, V, bias, exp = _p8_case()
+    L, T = K.shape[0], q.shape[0]
+    rng = np.random.default_rng(12)
+    got_o = np.zeros_like(exp[0])
+    got_l = np.zeros_like(exp[1])
+    for r in range(T):
+        i = L - T + r
+        for h in range(4):
+            s = K[:i + 1, 0] @ q[r, h] / np.sqrt(128) + bias[h, np.minimum(i - np.arange(i + 1), 399)]
+            lam = 2.0 ** rng.uniform(0.0, 8.0)
+            pr = oracle.fp8.e4m3_value(oracle.fp8.e4m3_code(lam * np.exp(s - s.max())))
+            got_o[r, h] = (pr @ V[:i + 1, 0]) / pr.sum()
+            got_l[r, h] = s.max() + np.log(pr.sum() / lam)
+    check_p8(_bf16(got_o), got_l, exp)
+
+
+def test_p8_checker_rejects_a_dropped_key_tile():
+    # the oracle's own result without one 64-key tile in the middle of the keys
+    q, K, V, bias, exp = _p8_case()
+    L, T = K.shape[0], q.shape[0]
+    parts = [oracle.relattn_rows(q, np.arange(L - T, L), K, V, bias, 0, 4, key_lo=0, key_hi=384),
+             oracle.relattn_rows(q, np.arange(L - T, L), K, V, bias, 0, 4, key_lo=448)]
+    o, l = oracle.lse_merge(parts)
+    with pytest.raises(AssertionError):
+        check_p8(_bf16(o), l, exp)
