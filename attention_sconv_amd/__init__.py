@@ -11,6 +11,9 @@
   ``inkattn_relattn_prefill_fp8`` -- the sconv cache write, the (multi-query)
                                  decode and the prefill with an FP8 (OCP
                                  E4M3, scaled) KV cache;
+* ``inkattn_relattn_prefill_fp8_mma`` -- the prefill over an E4M3 cache with
+                                 FP8 matrix products (Q and P rounded to E4M3),
+                                 for the global-attention layers;
 * ``inkattn_relattn_prefill``  -- relative-position GQA attention over new
                                  tokens (bf16/fp32 MFMA, sheared bias band);
 * ``inkattn_relattn_decode``   -- split-K paged decode plus log-sum-exp merge;
@@ -38,6 +41,7 @@ from ._lib import (  # noqa: F401
     inkattn_relattn_decode_mq, inkattn_relattn_decode_mq_num_splits,
     inkattn_relattn_decode_mq_workspace_size,
     inkattn_relattn_prefill_fp8, inkattn_relattn_prefill_fp8_workspace_size,
+    inkattn_relattn_prefill_fp8_mma,
     inkattn_probe_mfma_bf16, inkattn_probe_stream_read,
     PROBE_MFMA_WAVES, PROBE_MFMA_CHAINS, PROBE_READ_GROUPS,
 )

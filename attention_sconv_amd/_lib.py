@@ -27,6 +27,7 @@ EXPORTED = (
     "inkattn_relattn_prefill",
     "inkattn_relattn_prefill_fp8",
     "inkattn_relattn_prefill_fp8_workspace_size",
+    "inkattn_relattn_prefill_fp8_mma",
     "inkattn_relattn_decode_num_splits",
     "inkattn_relattn_decode_workspace_size",
     "inkattn_relattn_decode",
@@ -88,6 +89,9 @@ def _load():
     lib.inkattn_relattn_prefill_fp8.argtypes = [dp, i32, i32, i32, vp, vp, vp, f32, f32, vp,
                                                 i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.inkattn_relattn_prefill_fp8.restype = i32
+    lib.inkattn_relattn_prefill_fp8_mma.argtypes = [dp, i32, i32, i32, vp, vp, vp, f32, f32,
+                                                    vp, i32, vp, vp, vp, vp, vp, vp]
+    lib.inkattn_relattn_prefill_fp8_mma.restype = i32
     lib.inkattn_relattn_prefill_fp8_workspace_size.argtypes = [dp, i32, i32]
     lib.inkattn_relattn_prefill_fp8_workspace_size.restype = sz
     lib.inkattn_relattn_decode_num_splits.argtypes = [dp, i32, i32]
@@ -184,6 +188,18 @@ def inkattn_relattn_prefill_fp8(desc, num_seqs, num_tokens, max_q_len, q, k_cach
                                           _ptr(out), _ptr(lse), _ptr(workspace),
                                           workspace_bytes, _stream(stream))
     _check(st, "inkattn_relattn_prefill_fp8")
+
+
+def inkattn_relattn_prefill_fp8_mma(desc, num_seqs, num_tokens, max_q_len, q, k_cache, v_cache,
+                                    k_scale, v_scale, block_table, max_blocks_per_seq,
+                                    cu_seqlens_q, seq_lens, bias, out, lse=None, stream=None):
+    st = _lib.inkattn_relattn_prefill_fp8_mma(ctypes.byref(desc), num_seqs, num_tokens,
+                                              max_q_len, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                              k_scale, v_scale, _ptr(block_table),
+                                              max_blocks_per_seq, _ptr(cu_seqlens_q),
+                                              _ptr(seq_lens), _ptr(bias), _ptr(out), _ptr(lse),
+                                              _stream(stream))
+    _check(st, "inkattn_relattn_prefill_fp8_mma")
 
 
 def inkattn_relattn_decode_num_splits(desc, num_seqs, max_seq_len):

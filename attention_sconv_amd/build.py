@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libinkattn.so")
 SOURCES = ["api.hip", "sconv.hip", "decode.hip", "decode_mq.hip", "prefill.hip", "prefill_fp8.hip",
-           "probe.hip"]
+           "prefill_f8.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

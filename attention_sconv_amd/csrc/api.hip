@@ -321,6 +321,34 @@ inkattn_status_t inkattn_relattn_prefill_fp8(const inkattn_attn_desc_t* desc, in
                                           v_scale));
 }
 
+inkattn_status_t inkattn_relattn_prefill_fp8_mma(const inkattn_attn_desc_t* desc,
+                                                 int32_t num_seqs, int32_t num_tokens,
+                                                 int32_t max_q_len, const void* q,
+                                                 const void* k_cache, const void* v_cache,
+                                                 float k_scale, float v_scale,
+                                                 const int32_t* block_table,
+                                                 int32_t max_blocks_per_seq,
+                                                 const int32_t* cu_seqlens_q,
+                                                 const int32_t* seq_lens, const void* bias,
+                                                 void* out, float* lse, void* stream) {
+  inkattn_status_t st = check_desc(desc);
+  if (st != INKATTN_OK) return st;
+  if (desc->dtype != INKATTN_BF16) return INKATTN_ENOTSUP;
+  if (!fp8_scale_ok(k_scale) || !fp8_scale_ok(v_scale)) return INKATTN_EINVAL;
+  if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0) return INKATTN_EINVAL;
+  if (num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return INKATTN_OK;
+  if (max_blocks_per_seq < 1) return INKATTN_EINVAL;
+  if (!q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !seq_lens || !bias || !out)
+    return INKATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return INKATTN_EINVAL;
+  if (bias_table_too_large(desc)) return INKATTN_ENOTSUP;
+  return from_hip(inkattn::launch_prefill_f8(shape_of(desc), num_seqs, max_q_len, q, k_cache,
+                                             v_cache, block_table, max_blocks_per_seq,
+                                             cu_seqlens_q, seq_lens, bias, out, lse,
+                                             (hipStream_t)stream, k_scale, v_scale));
+}
+
 int32_t inkattn_relattn_decode_num_splits(const inkattn_attn_desc_t* desc, int32_t num_seqs,
                                           int32_t max_seq_len) {
   if (check_desc(desc) != INKATTN_OK || num_seqs < 1 || max_seq_len < 1) return 1;

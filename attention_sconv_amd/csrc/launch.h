@@ -41,6 +41,13 @@ hipError_t launch_prefill(const AttnShape& s, int num_seqs, int max_q_len, const
                           const int32_t* cu_seqlens_q, const int32_t* seq_lens,
                           const void* bias, void* out, float* lse, hipStream_t stream,
                           float k_scale = 1.0f, float v_scale = 1.0f);
+// E4M3 cache with FP8 matrix products (prefill_f8.hip).
+hipError_t launch_prefill_f8(const AttnShape& s, int num_seqs, int max_q_len, const void* q,
+                          const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                          const void* bias, void* out, float* lse, hipStream_t stream,
+                          float k_scale = 1.0f, float v_scale = 1.0f);
 
 // Pages of an E4M3 cache that the prefill of each sequence attends, as bf16
 // codes (exact) in a workspace cache: sequence b's block blk goes to

@@ -169,6 +169,15 @@ class DeviceCase:
                                              self.cu, self.seq_lens, self.bias, self.out, None,
                                              self.pf8_ws, self.pf8_ws_bytes)
 
+    def prefill_fp8_mma(self):
+        c = self.case
+        self.ink.inkattn_relattn_prefill_fp8_mma(self.desc, len(c.q_lens), c.num_tokens,
+                                                 int(c.q_lens.max()), self.q, self.k_cache,
+                                                 self.v_cache, self.fp8[0], self.fp8[1],
+                                                 self.block_table, self.block_table.shape[1],
+                                                 self.cu, self.seq_lens, self.bias, self.out,
+                                                 None)
+
     def decode_mq(self):
         c = self.case
         self.ink.inkattn_relattn_decode_mq(self.desc, len(c.q_lens), c.num_tokens,

@@ -214,6 +214,36 @@ inkattn_status_t inkattn_relattn_prefill_fp8(const inkattn_attn_desc_t* desc, in
                                              void* out, float* lse, void* workspace,
                                              size_t workspace_bytes, void* stream);
 
+/* Prefill over an E4M3 cache with FP8 matrix products, for the global
+ * (full-causal) attention layers ([A] Roadmap: FP8 for global attention,
+ * whose cost is compute as well as KV capacity).  The same logits as
+ * inkattn_relattn_prefill_fp8, computed with both products in E4M3:
+ *   - Q is quantised per tile of 256 query rows of one q-head (rows
+ *     256t .. 256t+255 of each sequence's chunk): s_q = amax / 448 over the
+ *     tile's |q| (1 for an all-zero tile), codes = RNE_E4M3(q * (448 / amax))
+ *     computed in fp32; the logits use code * s_q.
+ *   - The softmax probabilities (each <= 256) are rounded to E4M3 before the
+ *     P V product, and the row sums add the rounded values.
+ * K and V are read as codes straight from the pages (no workspace).  Outputs
+ * differ from the exact attention over (code * s_q, k codes * k_scale,
+ * v codes * v_scale) only through the rounding of the probabilities: each
+ * weight of the output's weighted mean moves by a relative 2^-4 at most.
+ *   k_cache, v_cache: uint8 codes, [num_blocks][Hkv][128][128] and
+ *                     [num_blocks][Hkv][128 dims][128 tokens].
+ * Other arguments as inkattn_relattn_prefill.  INKATTN_ENOTSUP for an fp32
+ * desc or a bias table of 2 GiB or more; INKATTN_EINVAL for a scale that is
+ * not positive and finite or a pointer that is not 16-byte aligned. */
+inkattn_status_t inkattn_relattn_prefill_fp8_mma(const inkattn_attn_desc_t* desc,
+                                                 int32_t num_seqs, int32_t num_tokens,
+                                                 int32_t max_q_len, const void* q,
+                                                 const void* k_cache, const void* v_cache,
+                                                 float k_scale, float v_scale,
+                                                 const int32_t* block_table,
+                                                 int32_t max_blocks_per_seq,
+                                                 const int32_t* cu_seqlens_q,
+                                                 const int32_t* seq_lens, const void* bias,
+                                                 void* out, float* lse, void* stream);
+
 /* Number of KV splits inkattn_relattn_decode uses for num_splits = 0 (auto):
  * enough (sequence, kv-head, split) work-groups to fill the GPU, never more
  * splits than 128-token blocks in the attended range ([A] FA4 with sheared

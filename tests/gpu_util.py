@@ -182,6 +182,21 @@ class GpuCase:
                                         out, lse, ws, ws_bytes, stream)
         return out, lse
 
+    def prefill_fp8_mma(self, with_lse=True, stream=None):
+        """inkattn_relattn_prefill_fp8_mma over all new tokens of every sequence."""
+        c = self.case
+        B = len(c.q_lens)
+        d = self.desc()
+        mb = self.block_table.shape[1]
+        out = torch.empty_like(self.q)
+        lse = (torch.empty((c.num_tokens, c.num_q_heads), dtype=torch.float32, device="cuda")
+               if with_lse else None)
+        ink.inkattn_relattn_prefill_fp8_mma(d, B, c.num_tokens, int(c.q_lens.max()), self.q,
+                                            self.k_cache, self.v_cache, self.fp8[0],
+                                            self.fp8[1], self.block_table, mb, self.cu,
+                                            self.seq_lens, self.bias, out, lse, stream)
+        return out, lse
+
     def decode_mq(self, num_splits=0, with_lse=True, stream=None):
         """All new tokens of every sequence in one multi-query decode call."""
         c = self.case

@@ -380,3 +380,28 @@ def test_prefill_fp8_rejects_fp32_and_sizes_workspace():
         2 * pages * 4 * 128 * 128 * 2 + (pages * 4 + 15) // 16 * 16
     assert ink.inkattn_relattn_prefill_fp8_workspace_size(
         ink.make_desc(ink.FP32, 32, 4, 0, 128), 3, 10) == 0
+
+
+def _prefill_fp8_mma(desc, **kw):
+    args = dict(num_seqs=2, num_tokens=5, max_q_len=4, q=FAKE, k=FAKE, v=FAKE, ks=0.5, vs=0.25,
+                bt=FAKE, mb=4, cu=FAKE, sl=FAKE, bias=FAKE, out=FAKE, lse=None)
+    args.update(kw)
+    return ink._lib._lib.inkattn_relattn_prefill_fp8_mma(
+        ctypes.byref(desc), args["num_seqs"], args["num_tokens"], args["max_q_len"], args["q"],
+        args["k"], args["v"], args["ks"], args["vs"], args["bt"], args["mb"], args["cu"],
+        args["sl"], args["bias"], args["out"], args["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_seqs=0), ink.OK), (dict(num_tokens=0), ink.OK), (dict(max_q_len=0), ink.OK),
+    (dict(ks=0.0), ink.EINVAL), (dict(vs=-1.0), ink.EINVAL), (dict(ks=float("inf")), ink.EINVAL),
+    (dict(ks=float("nan")), ink.EINVAL), (dict(mb=0), ink.EINVAL), (dict(q=None), ink.EINVAL),
+    (dict(k=FAKE + 8), ink.EINVAL), (dict(out=FAKE + 2), ink.EINVAL), (dict(num_seqs=-1), ink.EINVAL),
+])
+def test_prefill_fp8_mma_host_validation(kw, status):
+    d = ink.make_desc(ink.BF16, 32, 4, 0, 128)
+    assert _prefill_fp8_mma(d, **kw) == status
+
+
+def test_prefill_fp8_mma_rejects_fp32():
+    assert _prefill_fp8_mma(ink.make_desc(ink.FP32, 32, 4, 0, 128)) == ink.ENOTSUP
