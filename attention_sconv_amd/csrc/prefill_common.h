@@ -38,6 +38,15 @@ __device__ __forceinline__ void lds_dma16x4(u32x4 rsrc, uint32_t lds, uint32_t v
                "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
                :: "s"(lds), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(rsrc), "s"(soff) : "memory");
 }
+// Three such loads under one M0 value (instruction offsets 0, 1024, 2048).
+__device__ __forceinline__ void lds_dma16x3(u32x4 rsrc, uint32_t lds, uint32_t v0, uint32_t v1,
+                                            uint32_t v2, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\t"
+               "buffer_load_dwordx4 %1, %4, %5 offen lds\n\t"
+               "buffer_load_dwordx4 %2, %4, %5 offen offset:1024 lds\n\t"
+               "buffer_load_dwordx4 %3, %4, %5 offen offset:2048 lds"
+               :: "s"(lds), "v"(v0), "v"(v1), "v"(v2), "s"(rsrc), "s"(soff) : "memory");
+}
 // An empty asm that reads a fragment: forces its load to have completed here.
 __device__ __forceinline__ void keep_live(const Frag8<bf16>& f) { asm volatile("" :: "v"(f.v)); }
 __device__ __forceinline__ void keep_live(const Frag8<float>& f) {

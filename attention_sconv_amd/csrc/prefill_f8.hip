@@ -17,8 +17,8 @@
 //   (s_q * k_scale).
 // * P: the probabilities of the online softmax (<= 2^8 under the lazy
 //   rescale) are rounded to E4M3 for the PV product, and the row sums add
-//   the rounded values, so the output is a weighted mean with exactly the
-//   weights the product used.
+//   the rounded values (a product with a matrix of ones), so the output is a
+//   weighted mean with exactly the weights the product used.
 //
 // Schedule: as the bf16 prefill (prefill.hip): 8 waves, 32 query rows each,
 // ping-pong matrix and softmax phases between the two waves of a SIMD, K and
@@ -57,8 +57,11 @@ constexpr int kF8VSlots = kF8VRow / 16, kF8VData = kF8BK / 16;
 constexpr int kF8KLoads = kF8BK * kF8KSlots / 64;      // 9 wave loads per K tile
 constexpr int kF8VLoads = kHeadDim * kF8VSlots / 64;   // 10 per V^T tile
 constexpr int kF8Loaders = kF8Waves / 2;
-constexpr int kF8KPer = (kF8KLoads + kF8Loaders - 1) / kF8Loaders;
-constexpr int kF8VPer = (kF8VLoads + kF8Loaders - 1) / kF8Loaders;
+// Tile blocks per loader: loaders 0-2 take runs of three consecutive 1 KiB
+// blocks of K and of V^T (one M0 value per run: rewriting M0 costs the
+// issuing wave ~110 cycles per load); loader 3 takes V^T block 9.
+constexpr int kF8Run = 3;
+static_assert(kF8KLoads == 3 * kF8Run && kF8VLoads == 3 * kF8Run + 1, "run layout of the tiles");
 constexpr int kF8BandRaw = ((kF8Band + 2) / 2 + 63) / 64 * 64;  // dwords of a raw bf16 slice
 constexpr int kF8BandLoads = kF8BandRaw / 64;
 constexpr int kF8BandPer = (kF8BandLoads + kF8Loaders - 1) / kF8Loaders;
@@ -126,13 +129,6 @@ __device__ __forceinline__ uint32_t f8x4_probs(float a, float b, float c, float 
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
-// Sum of the four E4M3 values of a word.
-__device__ __forceinline__ float f8x4_sum(uint32_t w) {
-  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  return (lo[0] + lo[1]) + (hi[0] + hi[1]);
-}
-
 __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A) {
   __shared__ PrefillF8Smem sm;
 
@@ -187,6 +183,13 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
   auto page_rsrc = [&](const uint8_t* cache, int phys) {
     return make_buf_rsrc(cache + ((size_t)phys * A.Hkv + kvg) * (size_t)kPageBytes, kPageBytes);
   };
+  auto page_rsrc_early = [&](const uint8_t* cache, int phys) {   // starts 4 KiB before the page
+    return make_buf_rsrc(cache + ((size_t)phys * A.Hkv + kvg) * (size_t)kPageBytes - 4096,
+                         kPageBytes + 4096u);
+  };
+  // Block j (0 .. kF8Run-1) of this loader's share, or -1.
+  auto k_block = [&](int j) { return lw < 3 ? kF8Run * lw + j : -1; };
+  auto v_block = [&](int j) { return lw < 3 ? kF8Run * lw + j : (j == 0 ? kF8VLoads - 1 : -1); };
   auto lds_addr = [](const void* p) {
     return (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
   };
@@ -224,26 +227,26 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
   };
   auto dma_tiles = [&](int x, int k_phys, int v_phys) {
     if (lw < 0) return;
-    if (x < n_t) {                            // K of tile x
+    const int ln = lane;
+    if (x < n_t && lw < 3) {                  // K of tile x: one run of three blocks
       const int jt = jt_lo + x;
-      const u32x4 r = page_rsrc(kc, k_phys);
       const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(jt * kF8BK % kPage) * kHeadDim);
-      const uint32_t lds = lds_addr(&sm.k[x & 1][0]);
-#pragma unroll
-      for (int j = 0; j < kF8KPer; ++j) {
-        const int n = lw + kF8Loaders * j;
-        if (n < kF8KLoads) lds_dma16(r, lds + 1024u * n, k_src(64 * n + lane), soff);
-      }
+      const int n0 = kF8Run * lw;
+      lds_dma16x3(page_rsrc_early(kc, k_phys), lds_addr(&sm.k[x & 1][0]) + 1024u * n0,
+                  k_src(64 * n0 + ln) + 4096u, k_src(64 * (n0 + 1) + ln) + 3072u,
+                  k_src(64 * (n0 + 2) + ln) + 2048u, soff);
     }
     if (x >= 1) {                             // V of tile x-1
       const int jt = jt_lo + x - 1;
-      const u32x4 r = page_rsrc(vc, v_phys);
       const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(jt * kF8BK % kPage));
       const uint32_t lds = lds_addr(&sm.vt[(x - 1) & 1][0]);
-#pragma unroll
-      for (int j = 0; j < kF8VPer; ++j) {
-        const int n = lw + kF8Loaders * j;
-        if (n < kF8VLoads) lds_dma16(r, lds + 1024u * n, v_src(64 * n + lane), soff);
+      if (lw < 3) {
+        const int n0 = kF8Run * lw;
+        lds_dma16x3(page_rsrc_early(vc, v_phys), lds + 1024u * n0, v_src(64 * n0 + ln) + 4096u,
+                    v_src(64 * (n0 + 1) + ln) + 3072u, v_src(64 * (n0 + 2) + ln) + 2048u, soff);
+      } else {
+        const int n = kF8VLoads - 1;
+        lds_dma16(page_rsrc(vc, v_phys), lds + 1024u * n, v_src(64 * n + ln), soff);
       }
     }
   };
@@ -260,20 +263,20 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
     if (x < n_t && jt_lo + x == jt_hi) {
       u32x4* buf = reinterpret_cast<u32x4*>(&sm.k[x & 1][0]);
 #pragma unroll
-      for (int j = 0; j < kF8KPer; ++j) {
-        const int n = lw + kF8Loaders * j;
+      for (int j = 0; j < kF8Run; ++j) {
+        const int n = k_block(j);
         const int slot = 64 * n + ln;
-        if (n < kF8KLoads && f8_row_key(slot / kF8KSlots) >= n_tail) buf[slot] = u32x4{0, 0, 0, 0};
+        if (n >= 0 && f8_row_key(slot / kF8KSlots) >= n_tail) buf[slot] = u32x4{0, 0, 0, 0};
       }
     }
     if (x >= 1 && jt_lo + x - 1 == jt_hi) {
       u32x4* buf = reinterpret_cast<u32x4*>(&sm.vt[(x - 1) & 1][0]);
 #pragma unroll
-      for (int j = 0; j < kF8VPer; ++j) {
-        const int n = lw + kF8Loaders * j;
+      for (int j = 0; j < kF8Run; ++j) {
+        const int n = v_block(j);
         const int slot = 64 * n + ln;
         const int ch = slot % kF8VSlots;
-        if (n < kF8VLoads && ch < kF8VData && 16 * (ch + 1) > n_tail)
+        if (n >= 0 && ch < kF8VData && 16 * (ch + 1) > n_tail)
           buf[slot] = keep_first_bytes(buf[slot], n_tail - 16 * ch);
       }
     }
@@ -301,8 +304,17 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
 
   // ---- running softmax state
   float m_used = -INFINITY;
-  float l_sum = 0.0f;
   f32x16 o[4];
+  // Row sums as one more product: a matrix of E4M3 ones times P^T puts the
+  // sum of the rounded probabilities of a query row in every register of its
+  // column, and rescales with O.  (On the vector ALU the decode and the adds
+  // cost ~40 instructions per tile in the softmax phase, which is the longer
+  // of the two phases.)
+  f32x16 lacc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lacc[r] = 0.0f;
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -320,14 +332,9 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
   // V buffer; the closing one (i = n_t) computes an S^T nobody reads.
   auto matrix_phase = [&](int i) {
     const int kb = i & 1, vb = (i - 1) & 1;
+    // LDS reads in the order the products need them (they return in order):
+    // block t's band and K fragments, then V^T.
     i32x8 kf[2][2], vf[4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        kf[t][ks] = lds_read32(&sm.k[kb][(32 * t + lq) * kF8KRow + 64 * ks + 32 * lg]);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) vf[dt] = lds_read32(&sm.vt[vb][(32 * dt + lq) * kF8VRow + 32 * lg]);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int v0 = (kF8BQ - 1) - a_row + 32 * lg + 16 * t;
@@ -338,25 +345,34 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[t][4 * q4 + e] = x[e];
       }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        kf[t][ks] = lds_read32(&sm.k[kb][(32 * t + lq) * kF8KRow + 64 * ks + 32 * lg]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) vf[dt] = lds_read32(&sm.vt[vb][(32 * dt + lq) * kF8VRow + 32 * lg]);
     if (rescale) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) asm("v_mul_f32 %0, %1, %0" : "+v"(o[dt][r]) : "v"(alpha));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) asm("v_mul_f32 %0, %1, %0" : "+v"(lacc[r]) : "v"(alpha));
       rescale = false;
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int t = s & 1, ks = s >> 1;
-      acc[t] = mfma32_f8(kf[t][ks], qf[ks], acc[t]);
-      o[s] = mfma32_f8(vf[s], pf, o[s]);
-    }
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) acc[t] = mfma32_f8(kf[t][ks], qf[ks], acc[t]);
+    lacc = mfma32_f8(ones, pf, lacc);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32_f8(vf[dt], pf, o[dt]);
   };
 
   // Softmax phase: online softmax in base 2 with a lazy rescale; P rounded
-  // to E4M3 and the row sum taken over the rounded values.
+  // to E4M3 (its row sum follows in the next matrix phase).
   auto softmax_phase = [&]() {
     float mx = -INFINITY;
 #pragma unroll
@@ -369,22 +385,17 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
     rescale = __any(need);
     if (rescale) {
       alpha = need ? fast_exp2(m_used - m_tile) : 1.0f;
-      l_sum *= alpha;
       m_used = need ? m_tile : m_used;
     }
     const float msub = m_used == -INFINITY ? 0.0f : m_used;
-    float ls[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int w = 0; w < 8; ++w) {             // word w: keys 32 lg + 4w .. +3
       const int t = w >> 2, r0 = 4 * (w & 3);
-      const uint32_t code = f8x4_probs(fast_exp2(acc[t][r0] * c - msub),
-                                           fast_exp2(acc[t][r0 + 1] * c - msub),
-                                           fast_exp2(acc[t][r0 + 2] * c - msub),
-                                           fast_exp2(acc[t][r0 + 3] * c - msub));
-      pf[w] = (int)code;
-      ls[w & 1] += f8x4_sum(code);
+      pf[w] = (int)f8x4_probs(fast_exp2(acc[t][r0] * c - msub),
+                              fast_exp2(acc[t][r0 + 1] * c - msub),
+                              fast_exp2(acc[t][r0 + 2] * c - msub),
+                              fast_exp2(acc[t][r0 + 3] * c - msub));
     }
-    l_sum += ls[0] + ls[1];
   };
 
   // V buffer 1 is read (times P^T = 0) by the first matrix phase.
@@ -485,7 +496,7 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
   if (half == 0) __syncthreads();
 
   // ---- epilogue: O^T register r of tile dt is dim 32dt + 8(r/4) + 4lg + r%4
-  const float lt = pair_sum(l_sum);
+  const float lt = lacc[0];                   // (every register holds the row sum)
   if (!row_ok) return;
   const float inv = A.v_scale / lt;
   bf16* op = static_cast<bf16*>(A.out) + ((size_t)(tok0 + row0 + a_row) * A.Hq + h) * kHeadDim;

@@ -10,8 +10,12 @@ kernel alone (HIP events on its launch stream); sconv = the K/V sconv and
 cache write alone, in GB/s.
 
 Further legs in the same JSON line:
+  prefill_32k_fp8_mma  the headline workload over an E4M3 KV cache with FP8
+                 matrix products (Q and P rounded to E4M3), against the FP8
+                 MFMA peak
   prefill_8k     the 8K sliding-window prefill step (T=8192, window 2048)
-  prefill_fp8    the same over an E4M3 KV cache
+  prefill_fp8    the same over an E4M3 KV cache (pages converted to bf16)
+  prefill_8k_fp8_mma  the 8K workload with FP8 matrix products
   decode         16K sliding-window decode (64 sequences, window 4096):
                  one-token sconv + split-K decode (+ merge when split)
   decode_1m      1M-context full-attention decode (4 sequences): split-K
@@ -49,6 +53,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "rel-attn prefill TFLOP/s & decode KV GB/s per MI355X (% of roofline)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 (E4M3) MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 HEAD_DIM = 128
 
@@ -529,6 +534,50 @@ def prefill_leg(torch, args, name, result_key=None, with_sconv_leg=True):
     return summary, dc, flop
 
 
+def prefill_fp8_mma_leg(torch, args, name, bf16_ms=None):
+    """sconv (E4M3 cache write, scales 1/64) + the prefill with FP8 matrix
+    products on a prefill workload.  The roofline is the FP8 (E4M3) MFMA
+    peak; ``time_vs_bf16`` compares with the bf16 prefill of the same
+    workload measured earlier in this run."""
+    import synth
+    wl = synth.WORKLOADS[name]
+    dc = DeviceCase(synth.workload_case(wl, seed=0), torch, fp8_scales=(1 / 64, 1 / 64))
+    flop = 4 * HEAD_DIM * valid_pairs(wl.q_len, wl.seq_len, wl.window) * wl.num_q_heads * wl.batch
+
+    def step(ev):
+        dc.sconv()
+        if ev is not None:
+            ev[0].record()
+        dc.prefill_fp8_mma()
+        if ev is not None:
+            ev[1].record()
+
+    print(f"[bench] prefill {wl.name}, E4M3 cache, FP8 products", file=sys.stderr, flush=True)
+    steady_clocks(torch, step, args.steady_s)
+    ms_step, ks = time_region(torch, step, None, args.steps, args.warmup)
+    ms = sum(ks) / len(ks)
+    tf = flop / (ms * 1e-3) / 1e12
+    srcs = ["attention_sconv_amd/csrc/prefill_f8.hip", "attention_sconv_amd/csrc/prefill_common.h",
+            "attention_sconv_amd/csrc/device_common.h"]
+    out = {
+        "workload": wl.name + " with an E4M3 KV cache (scales 1/64), Q and P rounded to E4M3",
+        "ms_per_step": round(ms_step, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(f"prefill_f8_{wl.name}.traffic.txt", srcs),
+                     "kernel": "prefill_f8_kernel", "ms": round(ms, 4),
+                     "ms_median": round(float(np.median(ks)), 4), "ms_min": round(min(ks), 4),
+                     "algorithmic_flop": flop},
+        "note": "inkattn_relattn_prefill_fp8_mma: v_mfma_f32_32x32x64_f8f6f4 for Q K^T and P V",
+    }
+    if bf16_ms:
+        out["time_vs_bf16"] = round(ms / bf16_ms, 3)
+    del dc
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_leg(torch, args, name, fp8=False, flush=True):
     """sconv (one token per sequence) + split-K decode + merge steps of a
     decode workload, bf16 cache or E4M3 cache (scales 1/64)."""
@@ -644,6 +693,9 @@ def main():
     }
     del dc
     torch.cuda.empty_cache()
+    if not args.no_fp8:
+        result["prefill_32k_fp8_mma"] = prefill_fp8_mma_leg(torch, args, "full_prefill_32k",
+                                                            head["roofline"]["ms"])
 
     # ---------------- the 8K sliding-window prefill (sconv + prefill)
     if not args.no_prefill_8k:
@@ -680,6 +732,8 @@ def main():
                 "note": "inkattn_relattn_prefill_fp8: page conversion to a bf16 workspace + "
                         "prefill kernel, both inside the timed call"}
             del fpd
+            result["prefill_8k_fp8_mma"] = prefill_fp8_mma_leg(torch, args, "swa_prefill_8k",
+                                                               p8["roofline"]["ms"])
         torch.cuda.empty_cache()
 
     # ---------------- decode: 16K sliding window (64 sequences)
