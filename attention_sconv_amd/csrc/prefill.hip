@@ -53,8 +53,7 @@ constexpr int kBQ = 32 * kWaves;         // query rows per work-group (32 per wa
 constexpr int kBK = 64;                  // keys per KV tile
 constexpr int kBand = kBQ + kBK - 1;     // 319 distinct distances per tile
 // Copy stride of the band in LDS: 336 words = 16 (mod 64), so the four
-// copies start 4 bank groups apart and the 16 lanes of a quarter-wave
-// (4 copies x 4 consecutive 16-byte groups) hit 16 distinct bank groups.
+// copies start 4 bank groups apart (the band reads count no bank conflicts).
 constexpr int kBandPad = 336;
 static_assert(kBandPad >= kBand + 1 && kBandPad % 64 == 16, "band copy stride");
 constexpr int kXcds = 8;
@@ -63,12 +62,13 @@ static_assert((kBQ - 1) % 4 == 3, "band copy selection assumes kBQ % 4 == 0");
 static_assert(kBand <= kThreads, "one band entry per thread");
 
 // LDS rows are padded by one 16-byte bf16 fragment: a K row is 272 B, a V^T
-// row 144 B.  ds_read_b128 is served a quarter-wave (16 lanes) at a time over
-// 64 banks; a quarter reads one fragment column from 16 distinct rows, and
-// with these strides row r starts 17r (K) or 9r (V^T) bank groups in, which
-// is 16 distinct groups mod 16.  Unlike an XOR swizzle, padding keeps every
-// fragment read at (per-lane base + compile-time offset), so the LDS reads
-// cost no address arithmetic.
+// row 144 B.  A half-wave reads one fragment column from 32 distinct rows,
+// which start at 16-byte slot 17r (K) or 9r (V^T): 32 distinct slots mod 32,
+// a pattern a probe of ds_read_b128 times at full rate (rows of an even slot
+// count run at two thirds of it).  The bank-conflict counter reads 0 for
+// this kernel.  Unlike an XOR swizzle, padding keeps every fragment read at
+// (per-lane base + compile-time offset), so the LDS reads cost no address
+// arithmetic.
 constexpr int kKStride = kHeadDim + 8;   // elements per K row in LDS
 constexpr int kVStride = kBK + 8;        // elements per V^T row in LDS
 

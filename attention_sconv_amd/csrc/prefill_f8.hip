@@ -283,23 +283,45 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
   };
   float bias_last;
   float band_mul = 0.0f;                      // sqrt(128) / (s_q k_scale), set in the prologue
-  auto band_store = [&](int x) {              // waves 0-3
-    if (x >= n_t) return;
+  // Band of stage x, written by waves 0-3 (256 threads, entries tid and
+  // tid + 256): the raw bias entries are read from LDS at the start of the
+  // softmax phase (band_fetch) and the four shifted copies written at its
+  // end (band_write), so the LDS latency overlaps the softmax.
+  constexpr int kBandPerThread = (kF8Band + kF8Threads / 2 - 1) / (kF8Threads / 2);
+  auto band_dist = [&](int x, int k) {
+    return P0 - (jt_lo + x) * kF8BK + (kF8BQ - 1) - (tid + (kF8Threads / 2) * k);
+  };
+  auto band_fetch = [&](int x, float (&bv)[kBandPerThread]) {
     const bf16* raw = reinterpret_cast<const bf16*>(&sm.braw[x & 1][0]);
     const int e0 = band_e0(x);
 #pragma unroll
-    for (int k = 0; k < (kF8Band + kF8Threads / 2 - 1) / (kF8Threads / 2); ++k) {
+    for (int k = 0; k < kBandPerThread; ++k) {
+      const int dist = band_dist(x, k);
+      // (an index inside the slice for every lane; entries past R-1 use bias_last)
+      const int idx = min(max(h * A.R + min(dist, A.R - 1) - e0, 0), 2 * kF8BandRaw - 1);
+      bv[k] = to_f32(raw[idx]);
+    }
+  };
+  auto band_write = [&](int x, const float (&bv)[kBandPerThread]) {
+    if (x >= n_t) return;
+#pragma unroll
+    for (int k = 0; k < kBandPerThread; ++k) {
       const int v = tid + (kF8Threads / 2) * k;
       if (v < kF8Band) {
-        const int dist = P0 - (jt_lo + x) * kF8BK + (kF8BQ - 1) - v;
+        const int dist = band_dist(x, k);
         const bool vis = dist >= 0 && (A.window == 0 || dist < A.window);
-        const float bv = dist > A.R - 1 ? bias_last : to_f32(raw[h * A.R + dist - e0]);
-        const float band_v = vis ? bv * band_mul : -INFINITY;
+        const float b = dist > A.R - 1 ? bias_last : bv[k];
+        const float band_v = vis ? b * band_mul : -INFINITY;
 #pragma unroll
-        for (int sh = 0; sh < 4; ++sh)
-          if (v - sh >= 0) sm.band[x & 1][sh][v - sh] = band_v;
+        for (int sh = 0; sh < 4; ++sh)            // (entries before a copy's start: a spare slot)
+          sm.band[x & 1][sh][v - sh >= 0 ? v - sh : kF8BandPad - 1] = band_v;
       }
     }
+  };
+  auto band_store = [&](int x) {
+    float bv[kBandPerThread];
+    band_fetch(x, bv);
+    band_write(x, bv);
   };
 
   // ---- running softmax state
@@ -476,8 +498,10 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
     if (i == n_t) break;
     if (half == 0) {
       __syncthreads();
+      float bv[kBandPerThread];
+      band_fetch(i + 1, bv);
       softmax_phase();
-      band_store(i + 1);
+      band_write(i + 1, bv);
       __syncthreads();
     } else {
       wait_all_loads();
