@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libinkattn.so")
-SOURCES = ["api.hip", "sconv.hip", "decode.hip", "decode_mq.hip", "prefill.hip", "prefill_fp8.hip",
+SOURCES = ["api.hip", "sconv.hip", "decode.hip", "decode_mq.hip", "decode_mqr.hip", "prefill.hip", "prefill_fp8.hip",
            "prefill_f8.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

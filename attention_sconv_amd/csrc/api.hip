@@ -15,7 +15,7 @@ using inkattn::AttnShape;
 namespace {
 
 constexpr int kDefaultCUs = 256;            // MI355X, when no device answers the query
-constexpr int kMaxDecodeQueries = 16;       // query tokens per sequence in one decode call
+constexpr int kMaxDecodeQueries = inkattn::kMaxMqTokens;  // query tokens per sequence in one decode call
 
 // Compute units of the current device: the split heuristic aims at about one
 // (sequence, kv-head, split) work-group per CU.  Read once per device.

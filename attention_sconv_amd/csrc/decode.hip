@@ -585,7 +585,12 @@ hipError_t launch_decode(const AttnShape& s, int num_seqs, int num_tokens, int m
   const int n_ct = decode_column_tiles(s.Hq / s.Hkv, max_q_len);
   const float ks = fp8_scales ? fp8_scales[0] : 1.0f;
   const float vs = fp8_scales ? fp8_scales[1] : 1.0f;
-  if (decode_uses_lds_mq(s.dtype, s.Hq / s.Hkv, max_q_len)) {
+  if (decode_uses_reg_mq(s.dtype, s.Hq / s.Hkv, max_q_len, s.Hq, s.bias_len)) {
+    launch_decode_mq_reg(s, num_seqs, num_splits, max_q_len, q, k_cache, v_cache, block_table,
+                         max_blocks_per_seq, cu_seqlens_q, seq_lens, bias, out, lse, part_o,
+                         part_lse, fp8_scales, stream);
+    if (num_splits > 1) launch_merge<bf16>(s, num_tokens, num_splits, part_o, part_lse, out, lse, stream);
+  } else if (decode_uses_lds_mq(s.dtype, s.Hq / s.Hkv, max_q_len)) {
     launch_decode_mq_lds(s, num_seqs, num_splits, q, k_cache, v_cache, block_table,
                          max_blocks_per_seq, cu_seqlens_q, seq_lens, bias, out, lse, part_o,
                          part_lse, fp8_scales, stream);

@@ -72,6 +72,21 @@ constexpr bool decode_uses_lds_mq(int dtype, int G, int max_q_len) {
   return dtype == kDtypeBf16 && decode_column_tiles(G, max_q_len) >= 2 &&
          decode_column_tiles(G, max_q_len) <= 8;
 }
+// Query tokens per sequence in one decode call.
+constexpr int kMaxMqTokens = 16;
+// Of those, bf16 queries with 2 .. 5 column tiles run the register-resident
+// multi-query kernel (decode_mqr.hip) when the bias band of a 32-key item
+// (G heads x 31 + max_q_len distances) fits its 6 staged entries per lane
+// and the bias table its 24-bit row offsets.
+constexpr int kMaxRegMqTiles = 5;
+constexpr int kMaxRegMqG = 16;
+constexpr int kRegMqBandEntries = 384;
+constexpr bool decode_uses_reg_mq(int dtype, int G, int max_q_len, long Hq, long R) {
+  return decode_uses_lds_mq(dtype, G, max_q_len) &&
+         decode_column_tiles(G, max_q_len) <= kMaxRegMqTiles && G <= kMaxRegMqG &&
+         max_q_len <= kMaxMqTokens && G * (31 + max_q_len) <= kRegMqBandEntries &&
+         Hq * R < (1L << 24);
+}
 // Work-groups per (split, kv-head, sequence).
 constexpr int decode_groups_per_pair(int dtype, int G, int max_q_len) {
   return decode_uses_lds_mq(dtype, G, max_q_len) ? 1 : decode_column_tiles(G, max_q_len);
@@ -93,5 +108,13 @@ void launch_decode_mq_lds(const AttnShape& s, int num_seqs, int num_splits, cons
                           const int32_t* seq_lens, const void* bias, void* out, float* lse,
                           float* part_o, float* part_lse, const float* fp8_scales,
                           hipStream_t stream);
+// The register-resident multi-query split kernel alone (no merge), for the
+// shapes decode_uses_reg_mq admits.
+void launch_decode_mq_reg(const AttnShape& s, int num_seqs, int num_splits, int max_q_len,
+                          const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                          const void* bias, void* out, float* lse, float* part_o,
+                          float* part_lse, const float* fp8_scales, hipStream_t stream);
 
 }  // namespace inkattn

@@ -804,11 +804,12 @@ def main():
             "frac": round(m_gbs / PEAK_HBM_GBS, 4),
             "tflops": round(4 * HEAD_DIM * m_pairs / (m_ms * 1e-3) / 1e12, 2),
             "traffic": recorded_traffic(
-                "decode_mq_bf16_swa_decode_16k_mtp9.traffic.txt",
-                ["attention_sconv_amd/csrc/decode_mq.hip",
+                "decode_mqr_bf16_swa_decode_16k_mtp9.traffic.txt",
+                ["attention_sconv_amd/csrc/decode_mqr.hip",
                  "attention_sconv_amd/csrc/device_common.h"]),
             "note": "inkattn_relattn_decode_mq; the 72 (token, head) columns of a kv-head "
-                    "group share one read of its K/V, staged through LDS",
+                    "group share one read of its K/V: each of 4 waves holds every column "
+                    "and a quarter of the keys, loaded straight into its registers",
         }
         if "decode" in result:
             result["decode_mtp"]["time_vs_one_token_decode"] = round(
@@ -839,6 +840,10 @@ def main():
                 "kv_bytes": m_kv_bytes // 2, "achieved": round(mf_gbs, 1), "unit": "GB/s",
                 "frac": round(mf_gbs / PEAK_HBM_GBS, 4),
                 "speedup_vs_bf16_cache": round(m_ms / mf_ms, 3),
+                "traffic": recorded_traffic(
+                    "decode_mqr_fp8_swa_decode_16k_mtp9.traffic.txt",
+                    ["attention_sconv_amd/csrc/decode_mqr.hip",
+                     "attention_sconv_amd/csrc/device_common.h"]),
                 "note": "inkattn_relattn_decode_fp8 on the same workload (E4M3 codes, "
                         "scales 1/64)"}
             del mf

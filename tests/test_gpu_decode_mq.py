@@ -129,3 +129,17 @@ def test_decode_mq_small_windows(W, R):
     # of later tokens' windows inside the same call
     case = synth.make_case("bf16", [9, 9, 4], [0, 300, 128], 32, 4, W, R, seed=45 + W)
     _run_and_check(case)
+
+
+@pytest.mark.parametrize("peak", [15.0, 50.0])
+@pytest.mark.parametrize("q_lens", [[9, 3, 9], [16, 12, 16]])
+def test_decode_mq_old_keys_far_above_the_newest(peak, q_lens):
+    # keys 1000 or more positions back get `peak` added to every logit, and
+    # the kernels meet them last (pages are taken newest first): the running
+    # softmax reference set by the first keys is then passed by 15 (22 in
+    # log2 units: probabilities far above 1) or by 50 (72 in log2 units: the
+    # register kernel recomputes its range from the exact column max).  9
+    # tokens x 8 heads run the register kernel, 16 the LDS-staged one.
+    case = synth.make_case("bf16", q_lens, [3000, 1100, 1500], 32, 4, 0, 2048, seed=48)
+    case.bias[:, 1000:] = synth.round_bf16(case.bias[:, 1000:] + np.float32(peak))
+    _run_and_check(case)
