@@ -143,3 +143,13 @@ def test_decode_mq_old_keys_far_above_the_newest(peak, q_lens):
     case = synth.make_case("bf16", q_lens, [3000, 1100, 1500], 32, 4, 0, 2048, seed=48)
     case.bias[:, 1000:] = synth.round_bf16(case.bias[:, 1000:] + np.float32(peak))
     _run_and_check(case)
+
+
+@pytest.mark.parametrize("Hq,Hkv,q_max", [(32, 4, 8), (32, 4, 6), (8, 4, 16), (4, 1, 16)])
+def test_decode_mq_register_kernel_column_tiles(Hq, Hkv, q_max):
+    # 4, 3, 2 and 4 column tiles of 16 (token, head) columns; contexts end on
+    # and off page edges and on every quarter of a page
+    q_lens = [q_max, 1, q_max - 1, 3, q_max]
+    ctx = [2048, 127, 4000 - q_max, 31, 96]
+    case = synth.make_case("bf16", q_lens, ctx, Hq, Hkv, 1024, 1024, seed=49 + Hq + q_max)
+    _run_and_check(case)

@@ -184,6 +184,28 @@ def test_decode_fp8_full_1m_full_size():
     _run_and_check(case, (1 / 64, 1 / 64), scale_aware=True)
 
 
+@pytest.mark.parametrize("Hq,Hkv,q_max", [(32, 4, 5), (32, 4, 8), (4, 1, 9), (32, 4, 9)])
+@pytest.mark.parametrize("W,R", [(0, 3000), (2048, 2048)])
+def test_decode_fp8_multi_query_column_tiles(Hq, Hkv, q_max, W, R):
+    # 3, 4, 3 and 5 column tiles of 16 (token, head) columns, the register-
+    # resident multi-query kernel over an E4M3 cache; contexts end on and off
+    # page edges and on every quarter of a page
+    q_lens = [q_max, 1, q_max - 1, 2, q_max]
+    ctx = [2048, 127, 4000 - q_max, 31, 96]
+    case = synth.make_case("bf16", q_lens, ctx, Hq, Hkv, W, R, seed=97 + Hq + q_max + W)
+    _run_and_check(case, (1 / 32, 1 / 64))
+
+
+def test_decode_fp8_mtp9_16k_sampled():
+    # the 16K sliding-window verification workload (64 sequences x 9 query
+    # tokens) over an E4M3 cache at full size; the oracle checks every token
+    # and head of 8 sequences spread over the batch
+    wl = synth.WORKLOADS["swa_decode_16k_mtp9"]
+    case = synth.workload_case(wl, seed=0, past_device="cuda")
+    _run_and_check(case, (1 / 64, 1 / 64), seqs=list(range(0, wl.batch, 9)) + [wl.batch - 1],
+                   scale_aware=True)
+
+
 def _run_prefill_and_check(case, scales):
     gc = GpuCase(case, fp8_scales=scales)
     gc.sconv()
