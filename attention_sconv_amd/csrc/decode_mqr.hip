@@ -94,9 +94,27 @@ template <> struct MqrSet<fp8e4> {
   bf16 bias[kBandSlots];
 };
 
-__device__ __forceinline__ float row_pair_max16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+// Max over the lane pairs (l, l ^ 16) and (l, l ^ 32), i.e. over the four
+// lane groups of a column.  v_permlane16_swap / v_permlane32_swap exchange
+// the two registers between the lane pair, so after each swap one register
+// holds lane l's value and the other its partner's.  Written as one asm
+// block: fmaxf would first quiet possibly signalling NaNs of the swapped
+// values, four more instructions per column tile (the logits here are
+// finite or -inf).  The two wait states before each swap cover its read of
+// a register the previous instruction wrote.
+__device__ __forceinline__ float col_max(float x) {
+  float t;
+  asm volatile(
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane16_swap_b32 %0, %1\n\t"
+      "v_max_f32 %0, %0, %1\n\t"
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "+v"(x), "=&v"(t));
+  return x;
 }
 
 __device__ __forceinline__ Frag8<bf16> as_frag(const u32x4& w) {
@@ -189,6 +207,17 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
     bsrc[i] = ((kvh * G + (ok ? e : 0)) * R) | (v << 24);   // R * Hq < 2^24 (host check)
   }
   float* const band = sm.band[wave];
+  // Each tile's band reads through an LDS pointer the compiler cannot see
+  // into: its 8 reads then take small immediate offsets from one register
+  // (the band array itself starts further into LDS than a ds_read2 offset
+  // reaches, and each pair of reads would add it anew).
+  typedef __attribute__((address_space(3))) const float lds_cfloat;
+  lds_cfloat* bptr[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    bptr[ct] = (lds_cfloat*)(band + boff[ct] - 7);
+    asm volatile("" : "+v"(bptr[ct]));
+  }
 
   // ---- loads of item u (page my_hi - 1 - u, keys 32 wave .. +31 of it).
   const rsrc_t bias_r = make_rsrc(bias, (uint32_t)((size_t)Hq * R * sizeof(bf16)));
@@ -313,7 +342,7 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
     };
     auto band_read = [&](int ct, float (&bv)[8]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bv[e] = band[boff[ct] - e];
+      for (int e = 0; e < 8; ++e) bv[e] = bptr[ct][7 - e];
     };
     auto softmax = [&](int ct, const f32x4 (&sa)[2], const float (&bv)[8]) {
       float x[8];
@@ -323,9 +352,8 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
         x[e] = sa[e >> 2][e & 3] * c + bv[e];
         mx = fmaxf(mx, x[e]);
       }
-      mx = row_pair_max16(mx);
-      mx = pair_max(mx);
-      m_all[ct] = fmaxf(m_all[ct], mx);
+      mx = col_max(mx);
+      m_all[ct] = m_all[ct] > mx ? m_all[ct] : mx;
       m[ct] = m[ct] == -INFINITY ? mx : m[ct];
       over_lane = over_lane || mx > m[ct] + kBail;
       const float m_sub = m[ct] == -INFINITY ? 0.0f : m[ct];
