@@ -206,6 +206,17 @@ def test_decode_fp8_mtp9_16k_sampled():
                    scale_aware=True)
 
 
+@pytest.mark.parametrize("peak", [15.0, 50.0])
+def test_decode_fp8_multi_query_old_keys_far_above_the_newest(peak):
+    # as in the bf16-cache test: keys 1000 or more positions back get `peak`
+    # added to their logits and are met last, so the register kernel's
+    # softmax reference is passed by 22 or 72 (log2 units), the second
+    # through a rerun from the exact column max
+    case = synth.make_case("bf16", [9, 3, 9], [3000, 1100, 1500], 32, 4, 0, 2048, seed=98)
+    case.bias[:, 1000:] = synth.round_bf16(case.bias[:, 1000:] + np.float32(peak))
+    _run_and_check(case, (1 / 32, 1 / 32))
+
+
 def _run_prefill_and_check(case, scales):
     gc = GpuCase(case, fp8_scales=scales)
     gc.sconv()
