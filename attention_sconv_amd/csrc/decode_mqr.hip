@@ -384,12 +384,13 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
         for (int dt = 0; dt < 8; ++dt) o[step - 1][dt] = mfma16(vf[dt], pf, o[step - 1][dt]);
       }
       if (step < NCT) pf = softmax(step, sacc[step & 1], bv[step & 1]);
-      // LDS reads first, then one matrix product per five vector instructions.
+      // LDS reads first, then one matrix product per three vector
+      // instructions (2, 3, 5 and 8 measured within 1-2% of each other).
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
