@@ -39,6 +39,8 @@
 //   the end of each sequence) and the 8 q-heads of one GQA group land on the
 //   same XCD (hardware dispatches work-group ids round-robin over the 8
 //   XCDs), so they share K/V in that XCD's L2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "prefill_common.h"
@@ -426,8 +428,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   // LDS fragment reads run ahead of the MFMAs that consume them (K two
   // k-steps ahead, V one) and sched_barrier keeps the compiler from sinking
   // them back next to their uses.
-  auto matrix_phase = [&](int i) {
-    constexpr bool kQK = true, kPV = true;
+  // kQK false: the closing phase, PV of the last tile only (there is no
+  // tile n_t whose S^T would be computed).
+  auto matrix_phase = [&](int i, auto qk_tag) {
+    constexpr bool kQK = decltype(qk_tag)::value, kPV = true;
     const int kb = i & 1, vb = (i - 1) & 1;
     auto kfrag = [&](int ks, int t) {
       return Frag8<T>::load(&sm.k[kb][(32 * t + kp) * kKStride + 8 * (2 * ks + lg)]);
@@ -605,8 +609,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
   // staging work at all.
   if (half == 1) __syncthreads();                  // waves 4-7 sit out phase 0
   for (int i = 0;; ++i) {
-    matrix_phase(i);
-    if (i == n_t) break;
+    if (i == n_t) {
+      matrix_phase(i, std::false_type{});
+      break;
+    }
+    matrix_phase(i, std::true_type{});
     if (half == 0) {
       __syncthreads();                             // closes phase 2i
       softmax_phase();
