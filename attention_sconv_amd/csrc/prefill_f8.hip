@@ -34,6 +34,8 @@
 //   32g + 16t + 4a + c, so that accumulator register j of S^T block t in lane
 //   group g is key 32g + 16t + j: each lane group ends with the 32
 //   consecutive keys that its bytes of the P^T operand carry.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "prefill_common.h"
@@ -352,13 +354,16 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
   // Matrix phase of tile i: S^T_i = K_i Q^T from the band, and O^T +=
   // V^T_{i-1} P^T_{i-1}.  The first phase multiplies a zero P^T with a zeroed
   // V buffer; the closing one (i = n_t) computes an S^T nobody reads.
-  auto matrix_phase = [&](int i) {
+  // kQK false: the closing phase, PV of the last tile only (there is no
+  // tile n_t whose S^T would be computed).
+  auto matrix_phase = [&](int i, auto qk_tag) {
+    constexpr bool kQK = decltype(qk_tag)::value;
     const int kb = i & 1, vb = (i - 1) & 1;
     // LDS reads in the order the products need them (they return in order):
     // block t's band and K fragments, then V^T.
     i32x8 kf[2][2], vf[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2 && kQK; ++t) {
       const int v0 = (kF8BQ - 1) - a_row + 32 * lg + 16 * t;
       const float* bp = &sm.band[kb][band_shift][v0 - band_shift];
 #pragma unroll
@@ -384,10 +389,12 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
       rescale = false;
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kQK) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) acc[t] = mfma32_f8(kf[t][ks], qf[ks], acc[t]);
+        for (int ks = 0; ks < 2; ++ks) acc[t] = mfma32_f8(kf[t][ks], qf[ks], acc[t]);
+    }
     lacc = mfma32_f8(ones, pf, lacc);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32_f8(vf[dt], pf, o[dt]);
@@ -494,8 +501,11 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
   // ---- phase loop (the bf16 prefill's ping-pong)
   if (half == 1) __syncthreads();
   for (int i = 0;; ++i) {
-    matrix_phase(i);
-    if (i == n_t) break;
+    if (i == n_t) {
+      matrix_phase(i, std::false_type{});
+      break;
+    }
+    matrix_phase(i, std::true_type{});
     if (half == 0) {
       __syncthreads();
       float bv[kBandPerThread];
