@@ -136,7 +136,7 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
                        float v_scale) {
   constexpr bool kFp8 = std::is_same<TKV, fp8e4>::value;
   constexpr int kSz = (int)sizeof(TKV);
-  constexpr int kSets = kFp8 ? 3 : 2;
+  constexpr int kSets = 3;
   constexpr uint32_t kPageBytes = kPage * kHeadDim * kSz;
   __shared__ MqrSmem<NCT> sm;
 
