@@ -83,14 +83,16 @@ template <int NCT> struct MqrSmem {
 };
 
 // One item's loads: K fragments [t][ds], V^T fragments [dt] and the lane's
-// bias entries.  bf16: the 16-byte fragments themselves; E4M3: 8 codes each.
+// bias entries.  bf16: the 16-byte fragments themselves.  E4M3: K as 16 codes
+// per pair of k-steps [t][ds/2], V^T as 8 codes per fragment.
 template <typename TKV> struct MqrSet;
 template <> struct MqrSet<bf16> {
   u32x4 k[2][4], v[8];
   bf16 bias[kBandSlots];
 };
 template <> struct MqrSet<fp8e4> {
-  u32x2 k[2][4], v[8];
+  u32x4 k[2][2];
+  u32x2 v[8];
   bf16 bias[kBandSlots];
 };
 
@@ -168,8 +170,12 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
   const float c = 0.08838834764831845f * kLog2e * k_scale;   // log2(e) / sqrt(128)
 
   // ---- Q^T fragments to LDS: fragment (ct, ds), lane ln holds column
-  // 16ct + ln%16 (token = column / G, head = column % G), dims 32ds + 8(ln/16)
-  // .. +7.  Columns past n_cols are zero.
+  // 16ct + ln%16 (token = column / G, head = column % G) and the 8 dims of
+  // lane group g = ln/16 in k-step ds: 32ds + 8g .. +7 (bf16 cache), or
+  // 64(ds/2) + 16g + 8(ds%2) .. +7 (E4M3 cache).  The dot product may take
+  // the dims in any order that Q and K share; the E4M3 order gives each lane
+  // 16 consecutive K codes per pair of k-steps, one 16-byte load.  Columns
+  // past n_cols are zero.
 #pragma unroll
   for (int i = tid; i < NCT * 4 * 64; i += kRThreads) {
     const int ct = i >> 8, ds = (i >> 6) & 3, ln = i & 63;
@@ -177,8 +183,8 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
     u32x4 w = u32x4{0, 0, 0, 0};
     if (cc < n_cols) {
       const int token = cc / G, hh = kvh * G + cc % G;
-      w = *reinterpret_cast<const u32x4*>(q + ((size_t)(tok0 + token) * Hq + hh) * kHeadDim +
-                                          32 * ds + 8 * (ln >> 4));
+      const int d0 = kFp8 ? 64 * (ds >> 1) + 16 * (ln >> 4) + 8 * (ds & 1) : 32 * ds + 8 * (ln >> 4);
+      w = *reinterpret_cast<const u32x4*>(q + ((size_t)(tok0 + token) * Hq + hh) * kHeadDim + d0);
     }
     sm.q[i] = w;
   }
@@ -231,10 +237,10 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
     const int phys = block_table[(size_t)b * max_blocks + blk];
     return ((size_t)phys * Hkv + kvh) * (size_t)(kPage * kHeadDim);
   };
-  // K fragment (t, ds) of lane l: key 8(r/4) + 4t + r%4 (r = l%16), dims
-  // 32ds + 8grp .. +7.
+  // K fragment (t, ds) of lane l: key 8(r/4) + 4t + r%4 (r = l%16), the
+  // dims of lane group grp in k-step ds (the Q^T order above).
   const uint32_t k_voff =
-      (uint32_t)(((kItem * wave + 8 * (col >> 2) + (col & 3)) * kHeadDim + 8 * grp) * kSz);
+      (uint32_t)(((kItem * wave + 8 * (col >> 2) + (col & 3)) * kHeadDim + (kFp8 ? 16 : 8) * grp) * kSz);
   // V^T fragment dt of lane l: dim 16dt + l%16, keys 8grp .. +7 of the item.
   const uint32_t v_voff = (uint32_t)((col * kPage + kItem * wave + 8 * grp) * kSz);
   // Item u's loads: K, the bias entries of its band, V^T.  Items past the
@@ -246,13 +252,17 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
     const rsrc_t kr = make_rsrc(k_cache + base, bytes);
     const rsrc_t vr = make_rsrc(v_cache + base, bytes);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      if constexpr (kFp8) {
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) {
-        const uint32_t soff = (uint32_t)((4 * t * kHeadDim + 32 * ds) * kSz);
-        if constexpr (kFp8) st.k[t][ds] = buf_load8(kr, k_voff, soff);
-        else st.k[t][ds] = buf_load16(kr, k_voff, soff);
+        for (int j = 0; j < 2; ++j)
+          st.k[t][j] = buf_load16(kr, k_voff, (uint32_t)(4 * t * kHeadDim + 64 * j));
+      } else {
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds)
+          st.k[t][ds] = buf_load16(kr, k_voff, (uint32_t)((4 * t * kHeadDim + 32 * ds) * kSz));
       }
+    }
     const int d_min = pos0 - item_key0(u) - (kItem - 1);
 #pragma unroll
     for (int i = 0; i < kBandSlots; ++i) {
@@ -305,9 +315,18 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
     }
     Frag8<bf16> kf[2][4], vf[8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      if constexpr (kFp8) {
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) kf[t][ds] = as_frag(st.k[t][ds]);
+        for (int j = 0; j < 2; ++j) {
+          kf[t][2 * j] = fp8x8_to_bf16(st.k[t][j][0], st.k[t][j][1]);
+          kf[t][2 * j + 1] = fp8x8_to_bf16(st.k[t][j][2], st.k[t][j][3]);
+        }
+      } else {
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) kf[t][ds] = as_frag(st.k[t][ds]);
+      }
+    }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) vf[dt] = as_frag(st.v[dt]);
     if (key0 + kItem > L) {                      // (wave-uniform) keys past L in this item
