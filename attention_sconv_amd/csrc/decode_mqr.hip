@@ -210,7 +210,7 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
     const int e = s / bw, v = s - e * bw;
     const bool ok = s < G * bw;
     bdst[i] = ok ? band_base(e) + v : kBandFloats;   // (a spare float)
-    bsrc[i] = ((kvh * G + (ok ? e : 0)) * R) | (v << 24);   // R * Hq < 2^24 (host check)
+    bsrc[i] = ((kvh * G + (ok ? e : 0)) << 8) | v;          // bias row, offset v < 48
   }
   float* const band = sm.band[wave];
   // Each tile's band reads through an LDS pointer the compiler cannot see
@@ -266,9 +266,11 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
     const int d_min = pos0 - item_key0(u) - (kItem - 1);
 #pragma unroll
     for (int i = 0; i < kBandSlots; ++i) {
-      const int dist = min(max(d_min + (bsrc[i] >> 24), 0), R - 1);
-      st.bias[i] = buf_load_elem<bf16>(
-          bias_r, (uint32_t)(((bsrc[i] & 0xffffff) + dist) * (int)sizeof(bf16)));
+      const int dist = min(max(d_min + (bsrc[i] & 0xff), 0), R - 1);
+      // Row start as a 24-bit product (R < 2^24, host check); the whole
+      // table stays under 2^32 bytes, the buffer's offset range.
+      const uint32_t elem = __umul24((uint32_t)bsrc[i] >> 8, (uint32_t)R) + (uint32_t)dist;
+      st.bias[i] = buf_load_elem<bf16>(bias_r, elem * (uint32_t)sizeof(bf16));
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -309,7 +311,7 @@ void decode_mqr_kernel(int Hq, int Hkv, int window, int R, int S, int B,
     const int d_min = pos0 - key0 - (kItem - 1);
 #pragma unroll
     for (int i = 0; i < kBandSlots; ++i) {
-      const int d = d_min + (bsrc[i] >> 24);
+      const int d = d_min + (bsrc[i] & 0xff);
       const bool vis = d >= 0 && (window == 0 || d < window);
       band[bdst[i]] = vis ? to_f32(st.bias[i]) * kLog2e : -INFINITY;
     }

@@ -76,8 +76,8 @@ constexpr bool decode_uses_lds_mq(int dtype, int G, int max_q_len) {
 constexpr int kMaxMqTokens = 16;
 // Of those, bf16 queries with 2 .. 5 column tiles run the register-resident
 // multi-query kernel (decode_mqr.hip) when the bias band of a 32-key item
-// (G heads x 31 + max_q_len distances) fits its 6 staged entries per lane
-// and the bias table its 24-bit row offsets.
+// (G heads x 31 + max_q_len distances) fits its 6 staged entries per lane,
+// R fits a 24-bit multiply and the bias table a 32-bit byte offset.
 constexpr int kMaxRegMqTiles = 5;
 constexpr int kMaxRegMqG = 16;
 constexpr int kRegMqBandEntries = 384;
@@ -85,7 +85,7 @@ constexpr bool decode_uses_reg_mq(int dtype, int G, int max_q_len, long Hq, long
   return decode_uses_lds_mq(dtype, G, max_q_len) &&
          decode_column_tiles(G, max_q_len) <= kMaxRegMqTiles && G <= kMaxRegMqG &&
          max_q_len <= kMaxMqTokens && G * (31 + max_q_len) <= kRegMqBandEntries &&
-         Hq * R < (1L << 24);
+         R < (1L << 24) && Hq * R * 2 < (1L << 32);
 }
 // Work-groups per (split, kv-head, sequence).
 constexpr int decode_groups_per_pair(int dtype, int G, int max_q_len) {

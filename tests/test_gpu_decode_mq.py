@@ -153,3 +153,12 @@ def test_decode_mq_register_kernel_column_tiles(Hq, Hkv, q_max):
     ctx = [2048, 127, 4000 - q_max, 31, 96]
     case = synth.make_case("bf16", q_lens, ctx, Hq, Hkv, 1024, 1024, seed=49 + Hq + q_max)
     _run_and_check(case)
+
+
+def test_decode_mq_register_kernel_long_bias_table():
+    # R = 2^22 with 8 q-heads: 2^25 bias entries, so row starts lie past 2^24
+    # (full-attention layers verifying 9 tokens at a long context window)
+    q_lens = [9, 4, 9]
+    ctx = [3000, 130, 1000]
+    case = synth.make_case("bf16", q_lens, ctx, 8, 1, 0, 1 << 22, seed=53)
+    _run_and_check(case)

@@ -196,6 +196,13 @@ def test_decode_fp8_multi_query_column_tiles(Hq, Hkv, q_max, W, R):
     _run_and_check(case, (1 / 32, 1 / 64))
 
 
+def test_decode_fp8_multi_query_long_bias_table():
+    # R = 2^22 with 8 q-heads (2^25 bias entries, row starts past 2^24), the
+    # register-resident multi-query kernel over an E4M3 cache
+    case = synth.make_case("bf16", [9, 4, 9], [3000, 130, 1000], 8, 1, 0, 1 << 22, seed=98)
+    _run_and_check(case, (1 / 32, 1 / 64))
+
+
 def test_decode_fp8_mtp9_16k_sampled():
     # the 16K sliding-window verification workload (64 sequences x 9 query
     # tokens) over an E4M3 cache at full size; the oracle checks every token
