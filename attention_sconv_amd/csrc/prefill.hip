@@ -420,16 +420,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs A) {
 
   // Matrix phase of tile i: S^T_i = K_i Q^T (accumulators start as the
   // sheared bias band) and O^T += V^T_{i-1} P^T_{i-1}, interleaved two + two
-  // MFMAs per k-step.  Every matrix phase runs both products, which keeps one
-  // copy of the code: in the first, P^T is zero and V buffer 1 has been
-  // zeroed, so O gains exactly +0; the closing phase (i = n_t) computes a
-  // QK^T from whatever finite or stale data buffer n_t % 2 holds and nothing
-  // reads it.
+  // MFMAs per k-step.  In the first phase P^T is zero and V buffer 1 has
+  // been zeroed, so O gains exactly +0.
   // LDS fragment reads run ahead of the MFMAs that consume them (K two
   // k-steps ahead, V one) and sched_barrier keeps the compiler from sinking
   // them back next to their uses.
-  // kQK false: the closing phase, PV of the last tile only (there is no
-  // tile n_t whose S^T would be computed).
+  // kQK false: the closing phase (i = n_t), PV of the last tile only (there
+  // is no tile n_t whose S^T would be computed).
   auto matrix_phase = [&](int i, auto qk_tag) {
     constexpr bool kQK = decltype(qk_tag)::value, kPV = true;
     const int kb = i & 1, vb = (i - 1) & 1;

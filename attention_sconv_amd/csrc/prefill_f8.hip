@@ -353,9 +353,9 @@ __global__ __launch_bounds__(kF8Threads) void prefill_f8_kernel(PrefillF8Args A)
 
   // Matrix phase of tile i: S^T_i = K_i Q^T from the band, and O^T +=
   // V^T_{i-1} P^T_{i-1}.  The first phase multiplies a zero P^T with a zeroed
-  // V buffer; the closing one (i = n_t) computes an S^T nobody reads.
-  // kQK false: the closing phase, PV of the last tile only (there is no
-  // tile n_t whose S^T would be computed).
+  // V buffer.
+  // kQK false: the closing phase (i = n_t), PV of the last tile only (there
+  // is no tile n_t whose S^T would be computed).
   auto matrix_phase = [&](int i, auto qk_tag) {
     constexpr bool kQK = decltype(qk_tag)::value;
     const int kb = i & 1, vb = (i - 1) & 1;
